@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPTQ layer quantizer on one MI355X.
+
+One step = the whole hot path on one Llama-shaped layer with synthetic,
+seeded inputs already resident in HBM: H.zero_(), H += 2 X^T X over all
+calibration tokens (gptq_hessian_accumulate), then gptq_quantize_layer
+(damping, activation order, blocked Cholesky + inverse, the in-block
+quantize-and-compensate loop, the lazy trailing updates, bit packing).
+
+Metric: layer-quantize throughput in TFLOP/s of algorithmic work
+(F_H + F_upd) / t_step with F_H = n d_in (d_in + 1) (symmetric half of the
+Hessian) and F_upd = d_out d_in (d_in - 1) (all compensation FMAs x 2);
+ms_per_step is the layer time.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q_proj]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "hessian_product_q_proj_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_flops(wl):
+    f_h = wl.n * wl.d_in * (wl.d_in + 1)
+    f_upd = wl.d_out * wl.d_in * (wl.d_in - 1)
+    return f_h, f_upd
+
+
+def describe(wl):
+    return (f"{wl.name} {wl.d_out}x{wl.d_in} {wl.dtype}, n={wl.n} tokens, {wl.bits}-bit, group {wl.group_size}, "
+            f"block {wl.block_size}, act_order {'on' if wl.act_order else 'off'}")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("hessian.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "post_weight_quantization_04_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the Hessian product kernel from committed
+    rocprofv3 counter runs, or None when absent or taken on other source."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, W, X):
+    """The float64 oracle on a bounded sample of the same workload, scaled to
+    the whole layer: Hessian over n_s tokens (scaled by n / n_s), the inverse
+    factor at d_s channels (scaled by (d/d_s)^3) and the quantization loop on
+    r_s rows of a d_s-channel slice (scaled by (d_out/r_s) (d/d_s)^2)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle as O
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores, user_api="blas"):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        d_s = min(wl.d_in, 4096)
+        n_s = int(min(wl.n, max(512, 2.5e11 // (2 * d_s * d_s))))
+        r_s = min(wl.d_out, 64)
+        t0 = time.perf_counter()
+        H = O.hessian([X[:n_s, :d_s]], wl.dtype, d_s)
+        t_h = time.perf_counter() - t0
+        Hd = H + O.damping(H, wl.damp) * np.eye(d_s)
+        t0 = time.perf_counter()
+        O.inverse_cholesky_upper(Hd)
+        t_f = time.perf_counter() - t0
+        W0 = O.widen(W[:r_s, :d_s], wl.dtype)
+        t0 = time.perf_counter()
+        O.gptq(W0, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order)
+        t_g = time.perf_counter() - t0
+    t_loop = max(t_g - t_f, 0.0)
+    sc = wl.d_in / d_s
+    t_full = t_h * (wl.n / n_s) * sc * sc + t_f * sc ** 3 + t_loop * (wl.d_out / r_s) * sc * sc
+    f_h, f_upd = workload_flops(wl)
+    return {
+        "value": (f_h + f_upd) / t_full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "ms_per_layer_est": t_full * 1e3,
+        "sample": (f"float64 oracle: Hessian over {n_s} tokens x {d_s} channels ({t_h:.2f} s), inverse factor at "
+                   f"d={d_s} ({t_f:.2f} s), quantization loop on {r_s} rows x {d_s} channels ({t_loop:.2f} s); "
+                   f"scaled to the full layer ({wl.n} tokens, {wl.d_out}x{wl.d_in})"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="q_proj")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the quantizer runs on a single MI355X and this build has no "
+              "multi-GPU path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_04_amd as P
+    from post_weight_quantization_04_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    log(f"bench: generating {describe(wl)}")
+    t0 = time.perf_counter()
+    W = synth.make_w(wl)
+    X = synth.make_x(wl)
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s; copying to HBM")
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    Xd, Wd = to_dev(X), to_dev(W)
+    H = torch.zeros(wl.d_in, wl.d_in, dtype=torch.float32, device=dev)
+    code = P.BF16 if wl.dtype == "bf16" else P.F32
+    ws_h = torch.empty(max(P.hessian_workspace_size(wl.n, wl.d_in, code), 1), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(P.quantize_layer_workspace_size(wl.d_out, wl.d_in, wl.bits, wl.group_size, wl.block_size,
+                                                       wl.act_order), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        H.zero_()
+        P.hessian_accumulate(Xd, H, workspace=ws_h)
+        return P.quantize_layer(Wd, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order, workspace=ws_q)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"bench: warmup step {i + 1}/{args.warmup} done")
+    P.profile_enable(True)
+    P.profile_read(reset=True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    prof = P.profile_read(reset=True)
+    P.profile_enable(False)
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"bench: {args.steps} timed steps, {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
+
+    f_h, f_upd = workload_flops(wl)
+    value = (f_h + f_upd) / (ms_step * 1e-3) / 1e12
+    stages = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps} for k, v in prof.items()}
+    ms_h, n_h = prof["hessian_product"]
+    avg_h = ms_h / max(n_h, 1)
+    achieved = f_h / (avg_h * 1e-3) / 1e12 if n_h else None
+    traffic = measured_traffic()
+    roofline = {"kernel": "hess_bf16_kernel" if wl.dtype == "bf16" else "hess_f32_kernel",
+                "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                "frac": (achieved / (PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS)) if achieved else None,
+                "traffic": traffic, "avg_launch_ms": avg_h, "algorithmic_flops_per_launch": f_h}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the float64 oracle on a bounded sample")
+        cpu = cpu_baseline(wl, W, X)
+        log(f"bench: oracle {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "GPTQ layer-quantize ms + TFLOP/s (Hessian+update), 4096x4096, n=262144 tok",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16+fp32", "data": "synthetic",
+        "config": {"workload": describe(wl), "d_out": wl.d_out, "d_in": wl.d_in, "tokens": wl.n,
+                   "bits": wl.bits, "group_size": wl.group_size, "block_size": wl.block_size,
+                   "act_order": wl.act_order, "damp": wl.damp, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "flops": {"hessian": f_h, "update": f_upd},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * gptq.h -- C ABI of libgptq, a GPTQ layer quantizer for AMD MI355X (gfx950).
+ *
+ * The method (web pages on GPTQ, cited by page title and section):
+ *   - "GPTQ (GPT Quantization)" (brain.gartu.xyz), "Fondation theorique : OBQ":
+ *     H = 2 X^T X over calibration inputs; quantize a column, then move the
+ *     remaining columns by -e_i / (H^-1)_ii * (H^-1)_{i,F}.
+ *   - same page, "Algorithme complet (pseudo-code)": damp H with lambda*I,
+ *     invert through Cholesky, quantize in batches with a lazy update of the
+ *     later columns.
+ *   - "Optimization Gptq" (skillsdirectory.com), "Quantizacao group-wise" and
+ *     "Configuracoes de quantizacao": per-group scale and zero point; bits,
+ *     group_size, desc_act, damp_percent.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named X, W, H, Qpacked, scales, zeros, perm, workspace are
+ *     DEVICE pointers (HIP global memory); every size is in elements unless
+ *     it says bytes.  All matrices are row-major and densely packed.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it; calls return before the GPU finishes unless
+ *     stated otherwise.  The caller keeps every buffer alive until the stream
+ *     has passed the call.
+ *   - The caller owns all memory.  The library never allocates or frees
+ *     device memory.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     GPTQ_EINVAL nothing was launched and no output was written;
+ *     gptq_last_error() gives a detail string (thread-local).
+ *   - No C++ exception crosses this interface.
+ *   - Calls on different streams with distinct workspaces and outputs may run
+ *     concurrently.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define GPTQ_API __attribute__((visibility("default")))
+#else
+#define GPTQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPTQ_OK = 0,
+    GPTQ_EINVAL = 1,   /* bad argument (checked on the host, nothing launched) */
+    GPTQ_ENOTSPD = 2,  /* damped Hessian not positive definite (a pivot <= 0 or NaN) */
+    GPTQ_EHIP = 3,     /* a HIP runtime call failed */
+    GPTQ_ENOMEM = 4    /* workspace smaller than the size query returned */
+} gptq_status;
+
+typedef enum {
+    GPTQ_F32 = 0,      /* IEEE binary32 */
+    GPTQ_BF16 = 1      /* bfloat16 (upper 16 bits of a binary32) */
+} gptq_dtype;
+
+/* ---------------------------------------------------------------------------
+ * Stage 1: Hessian accumulation.
+ * "GPTQ (GPT Quantization)", sections "Fondation theorique : OBQ" and
+ * "Algorithme complet (pseudo-code)" step 1: H = 2 X^T X.
+ *
+ * Computes H[i][j] += 2 * sum_t X[t][i] * X[t][j] for all i, j.
+ *   X        device, [n][d_in] row-major, dtype x_dtype.  Products are formed
+ *            exactly and accumulated in fp32 (bf16 inputs on bf16 MFMA, fp32
+ *            inputs on fp32 MFMA).
+ *   H        device, [d_in][d_in] fp32.  Read and written (accumulated): zero
+ *            it before the first call.  Both triangles are written and the
+ *            result is bitwise symmetric if H was.
+ *   workspace device scratch of at least gptq_hessian_workspace_size(n, d_in,
+ *            x_dtype) bytes (may be NULL when that size is 0).
+ * n == 0 is a no-op.  Calling it on consecutive token chunks equals one call
+ * on their concatenation up to fp32 rounding; results are deterministic.
+ * Errors: EINVAL (null pointer, n < 0, d_in < 1, bad dtype), ENOMEM
+ * (workspace too small), EHIP.
+ * ------------------------------------------------------------------------- */
+GPTQ_API size_t gptq_hessian_workspace_size(int64_t n, int64_t d_in, gptq_dtype x_dtype);
+
+GPTQ_API gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, int64_t n, int64_t d_in,
+                                    float *H, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Stages 2-5: quantize one layer.
+ * "GPTQ (GPT Quantization)", "Algorithme complet (pseudo-code)" steps 1-3 and
+ * "Fondation theorique : OBQ"; "Optimization Gptq", "Quantizacao group-wise"
+ * and "Configuracoes de quantizacao" (bits, group_size, desc_act,
+ * damp_percent).
+ *
+ * Inputs (read-only):
+ *   W          device, [d_out][d_in], dtype w_dtype (one row per output
+ *              channel, one column per input channel).
+ *   H          device, [d_in][d_in] fp32, the undamped Hessian from stage 1.
+ *   bits       2, 3, 4 or 8.
+ *   group_size -1 (one group per row) or a multiple of 16; values >= d_in
+ *              also mean one group per row.  Unless one group spans the row,
+ *              block_size must be a multiple of group_size (or >= d_in).
+ *   block_size >= 1: columns per lazy batch (clamped to d_in).
+ *   damp       relative damping, lambda = damp * mean(diag H); finite, >= 0.
+ *   act_order  0: natural column order; 1: columns processed by descending
+ *              diag(H) (stable, ties to the lower index).
+ * Outputs (caller-allocated, device, all in processing order):
+ *   Qpacked    uint32 [gptq_packed_words(d_in, bits)][d_out].  Row r's codes
+ *              form a little-endian bit stream, code k at stream bits
+ *              [bits*k, bits*k + bits); word w holds stream bits [32w, 32w+32).
+ *   scales     fp32 [gptq_num_groups(d_in, group_size)][d_out].
+ *   zeros      fp32 [gptq_num_groups(d_in, group_size)][d_out], integers in
+ *              [0, 2^bits - 1].
+ *   perm       int32 [d_in]: perm[k] is the original column processed k-th.
+ *   Dequantization: W_hat[r][perm[k]] = scales[k/g][r] * (code(r,k) - zeros[k/g][r]).
+ * workspace   device scratch of at least gptq_quantize_layer_workspace_size(...)
+ *             bytes.
+ * The call synchronizes `stream` once, after the factorization, to read the
+ * positive-definiteness flag; everything after it is enqueued asynchronously.
+ * Errors: EINVAL, ENOMEM (nothing launched); ENOTSPD (outputs undefined);
+ * EHIP.
+ * ------------------------------------------------------------------------- */
+GPTQ_API size_t gptq_quantize_layer_workspace_size(int64_t d_out, int64_t d_in, int bits, int group_size,
+                                          int block_size, int act_order);
+
+GPTQ_API gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out, int64_t d_in,
+                                const float *H, int bits, int group_size, int block_size,
+                                float damp, int act_order,
+                                uint32_t *Qpacked, float *scales, float *zeros, int32_t *perm,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 2 alone, for inspection: activation order and the inverse factor.
+ * "Algorithme complet (pseudo-code)" steps 1-2 (damping, inverse through
+ * Cholesky).  Writes perm (int32 [d_in]) and U (fp32 [d_in][d_in], device):
+ * the upper Cholesky factor of (H[perm][:,perm] + lambda I)^-1, i.e.
+ * H_d^-1 = U^T U; entries below the diagonal are set to 0.  Uses the same
+ * workspace as gptq_quantize_layer (size query with d_out = 1).  Synchronizes
+ * `stream` once.  Errors as for gptq_quantize_layer.
+ * ------------------------------------------------------------------------- */
+GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float damp, int act_order,
+                                int32_t *perm, float *U, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage timing (tracing aid).  When enabled, every call records a pair of
+ * hipEvents around each stage's launches on the caller's stream; reading
+ * waits for those events and returns the summed GPU time per stage since the
+ * last reset.  Process-wide state: enable it only while one thread drives
+ * the library.  Stages:
+ *   0 hessian product kernel      1 hessian reduce/mirror kernel
+ *   2 damping, order and gathers   3 blocked Cholesky + inverse
+ *   4 flip to U                    5 in-block quantize kernels
+ *   6 trailing-update kernels      7 bit packing
+ * ------------------------------------------------------------------------- */
+#define GPTQ_NUM_STAGES 8
+typedef struct {
+    double ms[GPTQ_NUM_STAGES];        /* summed GPU milliseconds */
+    int64_t launches[GPTQ_NUM_STAGES]; /* timed launch groups */
+} gptq_profile;
+
+GPTQ_API void gptq_profile_enable(int on);
+GPTQ_API gptq_status gptq_profile_read(gptq_profile *out, int reset);
+GPTQ_API const char *gptq_profile_stage_name(int stage);
+
+/* Host-only helpers (no GPU work). */
+GPTQ_API int64_t gptq_packed_words(int64_t d_in, int bits);          /* ceil(bits*d_in/32), -1 if invalid */
+GPTQ_API int64_t gptq_num_groups(int64_t d_in, int group_size);      /* ceil(d_in/g), -1 if invalid */
+GPTQ_API const char *gptq_status_string(gptq_status s);
+GPTQ_API const char *gptq_last_error(void);                          /* detail of the last failure on this thread */
+GPTQ_API const char *gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H */

@@ -1,0 +1,246 @@
+"""GPTQ layer quantizer for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libgptq.so (include/gptq.h).  Every
+stage of the method runs in the library's HIP kernels; this module only
+allocates device memory and passes pointers and the current stream.  PyTorch
+is used for device memory and streams only.
+
+    H = torch.zeros(d_in, d_in, device="cuda")
+    hessian_accumulate(X, H)                       # H += 2 X^T X
+    q = quantize_layer(W, H, bits=4, group_size=128, block_size=128,
+                       damp=0.01, act_order=False)
+    q.qpacked, q.scales, q.zeros, q.perm
+
+The library must have been built (python -m post_weight_quantization_04_amd.build);
+the first call into it raises ImportError if libgptq.so is missing (there is
+no fallback path).  The seeded input generator (.synth) does not need it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "GptqError", "lib", "hessian_accumulate", "hessian_workspace_size", "quantize_layer",
+    "quantize_layer_workspace_size", "inverse_factor", "packed_words", "num_groups", "QuantizedLayer",
+    "LIB_PATH", "F32", "BF16", "profile_enable", "profile_read",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
+F32, BF16 = 0, 1
+_STATUS = {0: "GPTQ_OK", 1: "GPTQ_EINVAL", 2: "GPTQ_ENOTSPD", 3: "GPTQ_EHIP", 4: "GPTQ_ENOMEM"}
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libgptq.so not found at {LIB_PATH}; build it with "
+            "`python -m post_weight_quantization_04_amd.build` (there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    c = ctypes
+    L.gptq_hessian_workspace_size.argtypes = [c.c_int64, c.c_int64, c.c_int]
+    L.gptq_hessian_workspace_size.restype = c.c_size_t
+    L.gptq_hessian_accumulate.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_void_p,
+                                          c.c_void_p, c.c_size_t, c.c_void_p]
+    L.gptq_hessian_accumulate.restype = c.c_int
+    L.gptq_quantize_layer_workspace_size.argtypes = [c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int]
+    L.gptq_quantize_layer_workspace_size.restype = c.c_size_t
+    L.gptq_quantize_layer.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_void_p, c.c_int, c.c_int,
+                                      c.c_int, c.c_float, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
+                                      c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+    L.gptq_quantize_layer.restype = c.c_int
+    L.gptq_inverse_factor.argtypes = [c.c_void_p, c.c_int64, c.c_float, c.c_int, c.c_void_p, c.c_void_p,
+                                      c.c_void_p, c.c_size_t, c.c_void_p]
+    L.gptq_inverse_factor.restype = c.c_int
+    L.gptq_packed_words.argtypes = [c.c_int64, c.c_int]
+    L.gptq_packed_words.restype = c.c_int64
+    L.gptq_num_groups.argtypes = [c.c_int64, c.c_int]
+    L.gptq_num_groups.restype = c.c_int64
+    L.gptq_status_string.argtypes = [c.c_int]
+    L.gptq_status_string.restype = c.c_char_p
+    L.gptq_last_error.argtypes = []
+    L.gptq_last_error.restype = c.c_char_p
+    L.gptq_version.argtypes = []
+    L.gptq_version.restype = c.c_char_p
+    L.gptq_profile_enable.argtypes = [c.c_int]
+    L.gptq_profile_enable.restype = None
+    L.gptq_profile_read.argtypes = [c.POINTER(_Profile), c.c_int]
+    L.gptq_profile_read.restype = c.c_int
+    L.gptq_profile_stage_name.argtypes = [c.c_int]
+    L.gptq_profile_stage_name.restype = c.c_char_p
+    return L
+
+
+NUM_STAGES = 8
+
+
+class _Profile(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * NUM_STAGES), ("launches", ctypes.c_int64 * NUM_STAGES)]
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record hipEvents around every stage launch (see gptq_profile_enable)."""
+    _lib().gptq_profile_enable(int(bool(on)))
+
+
+def profile_read(reset: bool = True) -> dict:
+    """{stage name: (summed GPU ms, timed launch groups)} since the last reset."""
+    p = _Profile()
+    _check(_lib().gptq_profile_read(ctypes.byref(p), int(bool(reset))))
+    return {_lib().gptq_profile_stage_name(i).decode(): (p.ms[i], int(p.launches[i])) for i in range(NUM_STAGES)}
+
+
+_LIB = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GptqError(status, _lib().gptq_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch  # memory and streams only
+    return torch
+
+
+def _stream_ptr(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _require(t, name, dtype=None, ndim=None, device=True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def packed_words(d_in: int, bits: int) -> int:
+    return int(_lib().gptq_packed_words(d_in, bits))
+
+
+def num_groups(d_in: int, group_size: int) -> int:
+    return int(_lib().gptq_num_groups(d_in, group_size))
+
+
+def hessian_workspace_size(n: int, d_in: int, dtype_code: int) -> int:
+    return int(_lib().gptq_hessian_workspace_size(n, d_in, dtype_code))
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def hessian_accumulate(X, H, workspace=None, stream=None) -> None:
+    """H += 2 X^T X.  X: [n, d_in] float32/bfloat16 (device); H: [d_in, d_in] float32."""
+    torch = _torch()
+    _require(X, "X", ndim=2)
+    _require(H, "H", dtype=torch.float32, ndim=2)
+    n, d = X.shape
+    if H.shape != (d, d):
+        raise ValueError(f"H must be [{d}, {d}]")
+    code = _dtype_code(X)
+    ws = _workspace(hessian_workspace_size(n, d, code), X.device, workspace)
+    _check(_lib().gptq_hessian_accumulate(X.data_ptr() if n else None, code, n, d, H.data_ptr(),
+                                       ws.data_ptr() if ws is not None else None,
+                                       0 if ws is None else ws.numel(), _stream_ptr(stream)))
+
+
+def quantize_layer_workspace_size(d_out, d_in, bits, group_size, block_size, act_order) -> int:
+    return int(_lib().gptq_quantize_layer_workspace_size(d_out, d_in, bits, group_size, block_size, int(act_order)))
+
+
+@dataclass
+class QuantizedLayer:
+    qpacked: "object"   # uint32 words, torch.int32 view [words, d_out]
+    scales: "object"    # float32 [groups, d_out]
+    zeros: "object"     # float32 [groups, d_out]
+    perm: "object"      # int32 [d_in]
+    bits: int
+    group_size: int     # effective group size
+    d_in: int
+
+
+def quantize_layer(W, H, bits: int = 4, group_size: int = 128, block_size: int = 128, damp: float = 0.01,
+                   act_order: bool = False, workspace=None, stream=None) -> QuantizedLayer:
+    """Quantize one layer.  W: [d_out, d_in] float32/bfloat16; H: [d_in, d_in] float32 (undamped)."""
+    torch = _torch()
+    _require(W, "W", ndim=2)
+    _require(H, "H", dtype=torch.float32, ndim=2)
+    d_out, d_in = W.shape
+    if H.shape != (d_in, d_in):
+        raise ValueError(f"H must be [{d_in}, {d_in}]")
+    G = num_groups(d_in, group_size)
+    nw = packed_words(d_in, bits)
+    if G < 1 or nw < 0:
+        raise GptqError(1, "invalid group_size or bits")
+    dev = W.device
+    q = torch.empty((max(nw, 0), d_out), dtype=torch.int32, device=dev)
+    sc = torch.empty((G, d_out), dtype=torch.float32, device=dev)
+    zr = torch.empty((G, d_out), dtype=torch.float32, device=dev)
+    pm = torch.empty((d_in,), dtype=torch.int32, device=dev)
+    need = quantize_layer_workspace_size(d_out, d_in, bits, group_size, block_size, act_order)
+    ws = _workspace(need, dev, workspace)
+    _check(_lib().gptq_quantize_layer(W.data_ptr(), _dtype_code(W), d_out, d_in, H.data_ptr(), bits, group_size,
+                                   block_size, float(damp), int(bool(act_order)), q.data_ptr(), sc.data_ptr(),
+                                   zr.data_ptr(), pm.data_ptr(), ws.data_ptr() if ws is not None else None,
+                                   0 if ws is None else ws.numel(), _stream_ptr(stream)))
+    g_eff = d_in if (group_size == -1 or group_size >= d_in) else group_size
+    return QuantizedLayer(q, sc, zr, pm, bits, g_eff, d_in)
+
+
+def inverse_factor(H, damp: float = 0.01, act_order: bool = False, workspace=None, stream=None):
+    """(perm, U) with (H[perm][:, perm] + lambda I)^-1 = U^T U, U upper (stage 2 alone)."""
+    torch = _torch()
+    _require(H, "H", dtype=torch.float32, ndim=2)
+    d = H.shape[0]
+    pm = torch.empty((d,), dtype=torch.int32, device=H.device)
+    U = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    need = quantize_layer_workspace_size(1, d, 4, -1, 1, act_order)
+    ws = _workspace(need, H.device, workspace)
+    _check(_lib().gptq_inverse_factor(H.data_ptr(), d, float(damp), int(bool(act_order)), pm.data_ptr(),
+                                   U.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    return pm, U

@@ -1,0 +1,90 @@
+// Internal declarations shared by the HIP sources of libgptq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace gptq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// Hessian (hessian.hip)
+// ---------------------------------------------------------------------------
+struct HessPlan {
+    int tile;          // output tile edge (256 for bf16, 128 for fp32)
+    int nb;            // tile blocks along d_in
+    int ntiles;        // nb*(nb+1)/2 lower-triangle tiles
+    int s_off;         // token splits for off-diagonal tiles
+    int s_diag;        // token splits for diagonal tiles
+    int nwg;           // work groups of the product kernel
+    int64_t slots;     // partial tiles written (= nwg)
+};
+HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16);
+size_t hessian_ws_bytes(const HessPlan &p);
+// product kernel: lower tiles of X^T X per token split -> partial slots
+hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t d, float *partials,
+                                  const HessPlan &p, hipStream_t st);
+// H += 2 * (sum of a tile's slots in split order), mirrored to the upper triangle
+hipError_t hessian_reduce_launch(int64_t d, float *H, const float *partials, const HessPlan &p,
+                                 hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Preparation (prep.hip): diag / lambda, activation order, gathers
+// ---------------------------------------------------------------------------
+// diag(H) -> dg[d]; lam[0] = damp * mean(dg) (fixed-order reduction).
+hipError_t prep_diag_lambda(const float *H, int64_t d, float damp, float *dg, float *lam,
+                            hipStream_t st);
+// perm[rank(i)] = i with rank by descending dg, ties to the lower index
+// (identity when act_order == 0).  rank: int32 [d] scratch.
+hipError_t prep_perm(const float *dg, int64_t d, int act_order, int32_t *rank, int32_t *perm, hipStream_t st);
+// R[a][b] = H[p(a)][p(b)] (+lam on the diagonal) for a >= b, p(a) = perm[d-1-a].
+hipError_t prep_gather_h(const float *H, const int32_t *perm, const float *lam, int64_t d,
+                         float *R, hipStream_t st);
+// Wp[r][k] = W[r][perm[k]] as fp32.
+hipError_t prep_gather_w(const void *W, int is_bf16, const int32_t *perm, int64_t d_out,
+                         int64_t d_in, float *Wp, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Factorization (factor.hip): in-place lower Cholesky of R fused with the
+// lower triangular inverse, then the flip that yields U.
+// ---------------------------------------------------------------------------
+constexpr int FACT_NB = 128;
+hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t *info,
+                         hipStream_t st);
+// U[k][j] = M[d-1-k][d-1-j] for k < j (in place, upper triangle);
+// ud[k] = M[d-1-k][d-1-k]; uinv[k] = 1/ud[k].  zero_lower: clear the strictly
+// lower triangle afterwards (inspection output only).
+hipError_t factor_flip(float *R, int64_t d, float *ud, float *uinv, int zero_lower,
+                       hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Quantization loop (quant.hip, trail.hip) and packing (pack.hip)
+// ---------------------------------------------------------------------------
+struct QuantArgs {
+    float *Wp;             // [d_out][d_in] working weights (processing order)
+    const float *U;        // [d_in][d_in] upper factor (row-major, upper part valid)
+    const float *ud;       // [d_in] U diagonal
+    const float *uinv;     // [d_in] 1 / U diagonal
+    float *E;              // [B][d_out] block errors
+    uint8_t *codes;        // [d_in][d_out]
+    float *scales;         // [G][d_out]
+    float *zeros;          // [G][d_out]
+    int64_t d_out, d_in;
+    int bits, group, block;   // group: effective group size (d_in when one group)
+};
+size_t quant_lds_bytes(int block);
+hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st);
+hipError_t trail_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st);
+hipError_t pack_launch(const uint8_t *codes, int64_t d_out, int64_t d_in, int bits,
+                       uint32_t *Qpacked, hipStream_t st);
+
+}  // namespace gptq

@@ -1,0 +1,419 @@
+// Stage 1: H += 2 X^T X  ("GPTQ (GPT Quantization)", "Fondation theorique :
+// OBQ" definition of H and "Algorithme complet (pseudo-code)" step 1).
+//
+// X is row-major [n][d] and the contraction runs over tokens (rows).  The
+// product kernel computes lower-triangle output tiles of X^T X with the token
+// range split S ways; every work group writes its fp32 partial tile to a
+// scratch slot.  A second kernel sums the slots of each tile in split order
+// (deterministic, no float atomics), adds 2*sum into H and mirrors it to the
+// upper triangle through LDS so that H stays bitwise symmetric.
+//
+// bf16 path: 256x256 tiles, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16.
+// X is staged through LDS as loaded (token-major rows).  MFMA operands need 8
+// consecutive tokens of one channel per lane, so each lane reads four
+// channels of one token with ds_read_b64 for eight tokens and regroups the
+// 16-bit halves in registers.  MFMA output row i of operand slot m maps to
+// channel 4*i + m, which makes the four slots of a lane land on four adjacent
+// columns (one 16-byte store).
+//
+// fp32 path: 128x128 tiles, 4 waves of 64x64, v_mfma_f32_32x32x2_f32.
+#include "common.h"
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+namespace gptq {
+
+namespace {
+
+constexpr int BT = 256;   // bf16 tile
+constexpr int BBK = 32;   // tokens per LDS stage (bf16)
+constexpr int FT = 128;   // fp32 tile
+constexpr int FBK = 16;   // tokens per LDS stage (fp32)
+
+__device__ __forceinline__ void tile_coords(int t, int &I, int &J) {
+    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while (i * (i + 1) / 2 > t) --i;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    I = i;
+    J = t - i * (i + 1) / 2;
+}
+
+__device__ __forceinline__ unsigned lo_pair(unsigned a, unsigned b) {
+    return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ unsigned hi_pair(unsigned a, unsigned b) {
+    return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+// Load one 32-token x 256-channel bf16 slab (A or B operand) into registers.
+template <bool VEC>
+__device__ __forceinline__ void load_slab_bf16(const uint16_t *__restrict__ X, int64_t n, int d,
+                                               int64_t k, int c0, u32x4 (&r)[4]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = (tid >> 5) + 8 * p;
+        const int col = (tid & 31) * 8;
+        const int64_t t = k + row;
+        const int ch = c0 + col;
+        if (VEC) {
+            if (t < n && ch < d) {
+                r[p] = *(const u32x4 *)(X + t * (int64_t)d + ch);
+            } else {
+                r[p] = u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            unsigned w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                unsigned lo = 0, hi = 0;
+                if (t < n && ch + 2 * e < d) lo = X[t * (int64_t)d + ch + 2 * e];
+                if (t < n && ch + 2 * e + 1 < d) hi = X[t * (int64_t)d + ch + 2 * e + 1];
+                w[e] = lo | (hi << 16);
+            }
+            r[p] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+    }
+}
+
+__device__ __forceinline__ void store_slab_bf16(uint16_t *s, const u32x4 (&r)[4]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = (tid >> 5) + 8 * p;
+        const int col = (tid & 31) * 8;
+        *(u32x4 *)(s + row * BT + col) = r[p];
+    }
+}
+
+// Eight tokens (rows r0..r0+7) x four channels (c..c+3) -> four MFMA operands.
+__device__ __forceinline__ void frags_bf16(const uint16_t *s, int r0, int c, bf16x8 (&f)[4]) {
+    u32x2 v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = *(const u32x2 *)(s + (r0 + e) * BT + c);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        u32x4 q;
+        const int half = m >> 1;
+        if ((m & 1) == 0) {
+            q.x = lo_pair(v[0][half], v[1][half]);
+            q.y = lo_pair(v[2][half], v[3][half]);
+            q.z = lo_pair(v[4][half], v[5][half]);
+            q.w = lo_pair(v[6][half], v[7][half]);
+        } else {
+            q.x = hi_pair(v[0][half], v[1][half]);
+            q.y = hi_pair(v[2][half], v[3][half]);
+            q.z = hi_pair(v[4][half], v[5][half]);
+            q.w = hi_pair(v[6][half], v[7][half]);
+        }
+        f[m] = __builtin_bit_cast(bf16x8, q);
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256, 1) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n,
+                                                           int d, float *__restrict__ part, int ntiles,
+                                                           int64_t tok_per_split) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BBK * BT];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BBK * BT];
+
+    const int w = blockIdx.x;
+    const int split = w / ntiles;
+    int I, J;
+    tile_coords(w % ntiles, I, J);
+    const bool diag = (I == J);
+    const int64_t k0 = (int64_t)split * tok_per_split;
+    const int64_t k1 = std::min<int64_t>(n, k0 + tok_per_split);
+    const int nst = (k1 > k0) ? (int)((k1 - k0 + BBK - 1) / BBK) : 0;
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int h = lane >> 5, li = lane & 31;
+    // the wave above the diagonal of a diagonal tile has nothing to compute
+    const bool active = !(diag && wr < wc);
+
+    f32x16 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
+
+    const uint16_t *Bsrc_s[2] = {diag ? sA[0] : sB[0], diag ? sA[1] : sB[1]};
+    u32x4 ra[4], rb[4];
+    if (nst > 0) {
+        load_slab_bf16<VEC>(X, k1, d, k0, I * BT, ra);
+        if (!diag) load_slab_bf16<VEC>(X, k1, d, k0, J * BT, rb);
+        store_slab_bf16(sA[0], ra);
+        if (!diag) store_slab_bf16(sB[0], rb);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        const bool more = st + 1 < nst;
+        if (more) {
+            const int64_t k = k0 + (int64_t)(st + 1) * BBK;
+            load_slab_bf16<VEC>(X, k1, d, k, I * BT, ra);
+            if (!diag) load_slab_bf16<VEC>(X, k1, d, k, J * BT, rb);
+        }
+        if (active) {
+            const uint16_t *a = sA[buf];
+            const uint16_t *b = Bsrc_s[buf];
+#pragma unroll
+            for (int ks = 0; ks < BBK / 16; ++ks) {
+                bf16x8 fa[4], fb[4];
+                frags_bf16(a, ks * 16 + h * 8, wr * 128 + li * 4, fa);
+                frags_bf16(b, ks * 16 + h * 8, wc * 128 + li * 4, fb);
+#pragma unroll
+                for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        acc[ma * 4 + mb] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[mb], acc[ma * 4 + mb], 0, 0, 0);
+            }
+        }
+        if (more) {
+            store_slab_bf16(sA[buf ^ 1], ra);
+            if (!diag) store_slab_bf16(sB[buf ^ 1], rb);
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+    float *out = part + (int64_t)w * BT * BT;
+#pragma unroll
+    for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int r = wr * 128 + 4 * (8 * a + 4 * h + b) + ma;
+                const int c = wc * 128 + 4 * li;
+                f32x4 v = {acc[ma * 4 + 0][4 * a + b], acc[ma * 4 + 1][4 * a + b],
+                           acc[ma * 4 + 2][4 * a + b], acc[ma * 4 + 3][4 * a + b]};
+                *(f32x4 *)(out + r * BT + c) = v;
+            }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load_slab_f32(const float *__restrict__ X, int64_t n, int d, int64_t k,
+                                              int c0, f32x4 (&r)[2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int row = (tid >> 5) + 8 * p;
+        const int col = (tid & 31) * 4;
+        const int64_t t = k + row;
+        const int ch = c0 + col;
+        if (VEC) {
+            r[p] = (t < n && ch < d) ? *(const f32x4 *)(X + t * (int64_t)d + ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[p][e] = (t < n && ch + e < d) ? X[t * (int64_t)d + ch + e] : 0.f;
+        }
+    }
+}
+
+__device__ __forceinline__ void store_slab_f32(float *s, const f32x4 (&r)[2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int row = (tid >> 5) + 8 * p;
+        const int col = (tid & 31) * 4;
+        *(f32x4 *)(s + row * FT + col) = r[p];
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void hess_f32_kernel(const float *__restrict__ X, int64_t n, int d,
+                                                       float *__restrict__ part, int ntiles,
+                                                       int64_t tok_per_split) {
+    __shared__ __attribute__((aligned(16))) float sA[2][FBK * FT];
+    __shared__ __attribute__((aligned(16))) float sB[2][FBK * FT];
+    const int w = blockIdx.x;
+    const int split = w / ntiles;
+    int I, J;
+    tile_coords(w % ntiles, I, J);
+    const bool diag = (I == J);
+    const int64_t k0 = (int64_t)split * tok_per_split;
+    const int64_t k1 = std::min<int64_t>(n, k0 + tok_per_split);
+    const int nst = (k1 > k0) ? (int)((k1 - k0 + FBK - 1) / FBK) : 0;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int h = lane >> 5, li = lane & 31;
+    const bool active = !(diag && wr < wc);
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    f32x4 ra[2], rb[2];
+    if (nst > 0) {
+        load_slab_f32<VEC>(X, k1, d, k0, I * FT, ra);
+        store_slab_f32(sA[0], ra);
+        if (!diag) {
+            load_slab_f32<VEC>(X, k1, d, k0, J * FT, rb);
+            store_slab_f32(sB[0], rb);
+        }
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        const bool more = st + 1 < nst;
+        if (more) {
+            const int64_t k = k0 + (int64_t)(st + 1) * FBK;
+            load_slab_f32<VEC>(X, k1, d, k, I * FT, ra);
+            if (!diag) load_slab_f32<VEC>(X, k1, d, k, J * FT, rb);
+        }
+        if (active) {
+            const float *a = sA[buf];
+            const float *b = diag ? sA[buf] : sB[buf];
+#pragma unroll
+            for (int ks = 0; ks < FBK / 2; ++ks) {
+                const int row = 2 * ks + h;
+                float fa[2], fb[2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    fa[m] = a[row * FT + wr * 64 + m * 32 + li];
+                    fb[m] = b[row * FT + wc * 64 + m * 32 + li];
+                }
+#pragma unroll
+                for (int ma = 0; ma < 2; ++ma)
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+                        acc[ma * 2 + mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[ma], fb[mb], acc[ma * 2 + mb], 0, 0, 0);
+            }
+        }
+        if (more) {
+            store_slab_f32(sA[buf ^ 1], ra);
+            if (!diag) store_slab_f32(sB[buf ^ 1], rb);
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+    float *out = part + (int64_t)w * FT * FT;
+#pragma unroll
+    for (int ma = 0; ma < 2; ++ma)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int r = wr * 64 + ma * 32 + 8 * a + 4 * h + b;
+                    const int c = wc * 64 + mb * 32 + li;
+                    out[r * FT + c] = acc[ma * 2 + mb][4 * a + b];
+                }
+}
+
+// Sum the split partials of each lower tile (fixed order), H += 2*sum, mirror.
+// One work group per 64x64 sub-block.
+__global__ __launch_bounds__(256) void hess_reduce_kernel(const float *__restrict__ part, float *__restrict__ H,
+                                                          int d, int T, int ntiles, int nsplit) {
+    __shared__ float tileT[64][65];
+    const int sub_per = T / 64;
+    const int t = blockIdx.x / (sub_per * sub_per);
+    const int sb = blockIdx.x % (sub_per * sub_per);
+    const int sr = sb / sub_per, sc = sb % sub_per;
+    int I, J;
+    tile_coords(t, I, J);
+    const bool diag = (I == J);
+    if (diag && sr < sc) return;
+    const int row0 = I * T + sr * 64, col0 = J * T + sc * 64;
+    if (row0 >= d || col0 >= d) return;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int rr = ty; rr < 64; rr += 4) {
+        const int r = sr * 64 + rr, c = sc * 64 + tx;
+        const int gr = row0 + rr, gc = col0 + tx;
+        float v = 0.f;
+        if (gr < d && gc < d && !(diag && gc > gr)) {
+            float s = 0.f;
+            for (int sp = 0; sp < nsplit; ++sp) s += part[((int64_t)sp * ntiles + t) * T * T + (int64_t)r * T + c];
+            v = H[(int64_t)gr * d + gc] + 2.0f * s;
+            H[(int64_t)gr * d + gc] = v;
+        }
+        tileT[rr][tx] = v;
+    }
+    __syncthreads();
+    // mirror: H[col0 + cc][row0 + rr] = tileT[rr][cc]
+    for (int cc = ty; cc < 64; cc += 4) {
+        const int gr = col0 + cc, gc = row0 + tx;   // destination (upper triangle)
+        if (gr < d && gc < d && gc > gr) H[(int64_t)gr * d + gc] = tileT[tx][cc];
+    }
+}
+
+int cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            cached = cus;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
+}  // namespace
+
+HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16) {
+    HessPlan p{};
+    p.tile = is_bf16 ? BT : FT;
+    const int bk = is_bf16 ? BBK : FBK;
+    p.nb = (int)cdiv(d, p.tile);
+    p.ntiles = p.nb * (p.nb + 1) / 2;
+    const int cus = 256;   // planning assumes one work group per CU on a 256-CU part
+    // pick the token split that minimises rounds * per-group work + partial traffic
+    const double flop_rate_cu = 0.6 * (is_bf16 ? 2.5e15 : 1.57e14) / 256.0;
+    const double t_tok = 2.0 * p.tile * p.tile / flop_rate_cu;
+    const double bw = 4.0e12;
+    int best_s = 1;
+    double best = 1e300;
+    const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(32, cdiv(std::max<int64_t>(n, 1), 4 * bk)));
+    for (int s = 1; s <= smax; ++s) {
+        const int64_t nwg = (int64_t)s * p.ntiles;
+        const int64_t tok = cdiv(cdiv(std::max<int64_t>(n, 1), s), bk) * bk;
+        const double rounds = (double)cdiv(nwg, cus);
+        const double bytes = 2.0 * (double)nwg * p.tile * p.tile * 4.0;
+        const double t = rounds * tok * t_tok + bytes / bw;
+        if (t < best * 0.98) {
+            best = t;
+            best_s = s;
+        }
+    }
+    p.s_off = p.s_diag = best_s;
+    p.nwg = best_s * p.ntiles;
+    p.slots = p.nwg;
+    return p;
+}
+
+size_t hessian_ws_bytes(const HessPlan &p) {
+    return align256((size_t)p.slots * p.tile * p.tile * sizeof(float));
+}
+
+hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t d, float *partials,
+                                  const HessPlan &p, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    (void)cu_count;
+    const int bk = is_bf16 ? BBK : FBK;
+    const int64_t tok = cdiv(cdiv(n, p.s_off), bk) * bk;
+    if (is_bf16) {
+        if (d % 8 == 0)
+            hess_bf16_kernel<true><<<p.nwg, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, tok);
+        else
+            hess_bf16_kernel<false><<<p.nwg, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, tok);
+    } else {
+        if (d % 4 == 0)
+            hess_f32_kernel<true><<<p.nwg, 256, 0, st>>>((const float *)X, n, (int)d, partials, p.ntiles, tok);
+        else
+            hess_f32_kernel<false><<<p.nwg, 256, 0, st>>>((const float *)X, n, (int)d, partials, p.ntiles, tok);
+    }
+    return hipGetLastError();
+}
+
+hipError_t hessian_reduce_launch(int64_t d, float *H, const float *partials, const HessPlan &p, hipStream_t st) {
+    const int sub = p.tile / 64;
+    hess_reduce_kernel<<<p.ntiles * sub * sub, 256, 0, st>>>(partials, H, (int)d, p.tile, p.ntiles, p.s_off);
+    return hipGetLastError();
+}
+
+}  // namespace gptq

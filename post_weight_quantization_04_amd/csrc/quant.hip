@@ -1,0 +1,237 @@
+// Stage 3: the in-block sequential quantize-and-compensate loop.
+// "GPTQ (GPT Quantization)", "Fondation theorique : OBQ" (quantize column i,
+// take its error, move the remaining columns) and "Algorithme complet
+// (pseudo-code)" step 3 (columns in batches); "Optimization Gptq",
+// "Quantizacao group-wise" (per-group scale and zero point).
+//
+// For block columns [b, e) of the processing order and every row r:
+//   at a group start: xmin = min(0, min w), xmax = max(0, max w) over the
+//     group's current values (an all-zero group uses [0, 1]);
+//     s = (xmax - xmin) / maxq, z = rint(-xmin / s)
+//   for k = b .. e-1:  q = clamp(rint(w_k / s) + z, 0, maxq),
+//     E_k = (w_k - s (q - z)) / U_kk,  w_j -= E_k U_kj  for k < j < e.
+// The update of the columns after e is left to the trailing product.
+//
+// Layout: a work group owns 16 rows; each row is spread over one 16-lane DPP
+// row (lane c holds column c of the current 16-column chunk), so a wave
+// holds four rows.  The block's W tile and the upper part of the block's U
+// are staged in LDS.  Per column step the current value is broadcast across
+// the 16 lanes with DPP row_newbcast; every lane then computes the same
+// quantization and updates its own column.  After a chunk, its 16 errors
+// (held by every lane of the row) are applied to the rest of the block in
+// LDS with 4-column vector reads of W and U.
+#include "common.h"
+
+#include <algorithm>
+#include <utility>
+
+namespace gptq {
+
+namespace {
+
+constexpr int QROWS = 16;     // rows per work group
+constexpr int CH = 16;        // columns per chunk (= lanes per row)
+
+__host__ __device__ inline int roundup16(int x) { return (x + 15) & ~15; }
+
+// packed upper-triangle layout of the U block: row i keeps columns
+// [4*floor(i/4), Bp); offsets stay 16-byte aligned.
+__host__ __device__ inline int uoff(int i, int Bp) {
+    const int A = i >> 2, r = i & 3;
+    return 4 * A * Bp - 8 * A * (A - 1) + r * (Bp - 4 * A);
+}
+__host__ __device__ inline int usize(int Bp) { return uoff(Bp, Bp); }
+__device__ __forceinline__ int uidx(int i, int j, int Bp) { return uoff(i, Bp) + j - 4 * (i >> 2); }
+
+template <int S>
+__device__ __forceinline__ float bcast16(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + S, 0xF, 0xF, false));
+}
+
+struct Quantizer {
+    float s, inv_s, z, maxq;
+};
+
+__device__ __forceinline__ Quantizer make_quantizer(float xmin, float xmax, float maxq) {
+    xmin = fminf(xmin, 0.f);
+    xmax = fmaxf(xmax, 0.f);
+    if (xmax == xmin) xmax = 1.f;       // all-zero group
+    Quantizer Q;
+    Q.s = (xmax - xmin) / maxq;
+    Q.z = rintf(-xmin / Q.s);
+    Q.inv_s = 1.f / Q.s;
+    Q.maxq = maxq;
+    return Q;
+}
+
+__device__ __forceinline__ void minmax16(float &mn, float &mx) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+    }
+}
+
+struct StepCtx {
+    const float *Ul;
+    int Bp, c0, c, nb;
+    float *Erow;      // E values of the chunk (same in all 16 lanes of a row)
+};
+
+template <int S>
+__device__ __forceinline__ void qstep(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
+                                      const Quantizer &Q, const float *__restrict__ uinv_b) {
+    const int i = cx.c0 + S;
+    if (i >= cx.nb) return;                         // uniform: ragged last chunk
+    const float x = bcast16<S>(w);
+    const float t = x * Q.inv_s;
+    const float q = fminf(fmaxf(rintf(t) + Q.z, 0.f), Q.maxq);
+    const float wq = Q.s * (q - Q.z);
+    const float err = (x - wq) * uinv_b[i];
+    Ereg[S] = err;
+    if (cx.c == S) {
+        myq = q;
+        myE = err;
+    }
+    if (cx.c > S) w = fmaf(-err, cx.Ul[uidx(i, cx.c0 + cx.c, cx.Bp)], w);
+}
+
+template <int... S>
+__device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
+                                          const Quantizer &Q, const float *__restrict__ uinv_b,
+                                          std::integer_sequence<int, S...>) {
+    (qstep<S>(w, myq, myE, Ereg, cx, Q, uinv_b), ...);
+}
+
+// One launch per block [b, e).  Grid: ceil(d_out / 16) groups of 256 threads.
+__global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, int e) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int nb = e - b;
+    const int Bp = roundup16(nb);
+    const int LW = Bp + 4;                 // W tile row stride (floats)
+    float *Wl = lds;                       // [16][LW]
+    float *Ul = lds + QROWS * LW;          // packed upper U block
+    const int tid = threadIdx.x;
+    const int rl = tid >> 4, c = tid & 15;
+    const int64_t row0 = (int64_t)blockIdx.x * QROWS;
+    const int64_t row = row0 + rl;
+    const bool row_ok = row < a.d_out;
+    const int64_t d_in = a.d_in, d_out = a.d_out;
+
+    // stage W tile
+    for (int idx = tid; idx < QROWS * Bp; idx += 256) {
+        const int r = idx / Bp, j = idx % Bp;
+        const int64_t gr = row0 + r;
+        Wl[r * LW + j] = (gr < d_out && j < nb) ? a.Wp[gr * d_in + b + j] : 0.f;
+    }
+    // stage U block (upper part, packed)
+    {
+        const int wv = tid >> 6, ln = tid & 63;
+        for (int i = wv; i < nb; i += 4) {
+            const int j0 = 4 * (i >> 2);
+            const int base = uoff(i, Bp) - j0;
+            for (int j = j0 + ln; j < Bp; j += 64) {
+                float v = 0.f;
+                if (j > i && j < nb) v = a.U[(int64_t)(b + i) * d_in + b + j];
+                else if (j == i) v = a.ud[b + i];
+                Ul[base + j] = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    const float maxq = (float)((1 << a.bits) - 1);
+    const int g = a.group;
+    Quantizer Q{1.f, 1.f, 0.f, maxq};
+    if (b % g != 0) {
+        // the current group began in an earlier block: reuse its parameters
+        const int64_t gi = b / g;
+        const float s = row_ok ? a.scales[gi * d_out + row] : 1.f;
+        Q.s = s;
+        Q.inv_s = 1.f / s;
+        Q.z = row_ok ? a.zeros[gi * d_out + row] : 0.f;
+    }
+    const float *uinv_b = a.uinv + b;
+
+    for (int c0 = 0; c0 < nb; c0 += CH) {
+        const int k = b + c0;
+        if (k % g == 0) {
+            // group start: parameters from the current values of the group's columns
+            float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+            if (c0 == 0) {
+                const int gl = (int)std::min<int64_t>(g, d_in - k);
+                if (row_ok)
+                    for (int j = c; j < gl; j += CH) {
+                        const float v = a.Wp[row * d_in + k + j];
+                        mn = fminf(mn, v);
+                        mx = fmaxf(mx, v);
+                    }
+            } else {
+                const int gl = std::min(g, nb - c0);
+                for (int j = c; j < gl; j += CH) {
+                    const float v = Wl[rl * LW + c0 + j];
+                    mn = fminf(mn, v);
+                    mx = fmaxf(mx, v);
+                }
+            }
+            minmax16(mn, mx);
+            if (!row_ok) mn = mx = 0.f;
+            Q = make_quantizer(mn, mx, maxq);
+            if (row_ok && c == 0) {
+                const int64_t gi = k / g;
+                a.scales[gi * d_out + row] = Q.s;
+                a.zeros[gi * d_out + row] = Q.z;
+            }
+        }
+        float w = Wl[rl * LW + c0 + c];
+        float myq = 0.f, myE = 0.f;
+        float Ereg[CH];
+        StepCtx cx{Ul, Bp, c0, c, nb, nullptr};
+        run_chunk(w, myq, myE, Ereg, cx, Q, uinv_b, std::make_integer_sequence<int, CH>{});
+        if (row_ok && c0 + c < nb) {
+            a.codes[(int64_t)(k + c) * d_out + row] = (uint8_t)myq;
+            a.E[(int64_t)(c0 + c) * d_out + row] = myE;
+        }
+        // apply this chunk's errors to the rest of the block
+        const int jr = c0 + CH;
+        const int nsteps = std::min(CH, nb - c0);
+        for (int j = jr + 4 * c; j < nb; j += 4 * CH) {
+            f32x4 wv = *(const f32x4 *)(Wl + rl * LW + j);
+#pragma unroll
+            for (int s = 0; s < CH; ++s) {
+                if (s < nsteps) {
+                    const f32x4 u = *(const f32x4 *)(Ul + uidx(c0 + s, j, Bp));
+                    wv.x = fmaf(-Ereg[s], u.x, wv.x);
+                    wv.y = fmaf(-Ereg[s], u.y, wv.y);
+                    wv.z = fmaf(-Ereg[s], u.z, wv.z);
+                    wv.w = fmaf(-Ereg[s], u.w, wv.w);
+                }
+            }
+            *(f32x4 *)(Wl + rl * LW + j) = wv;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+size_t quant_lds_bytes(int block) {
+    const int Bp = roundup16(block);
+    return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp));
+}
+
+hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st) {
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t err = hipFuncSetAttribute((const void *)quant_block_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (err != hipSuccess) return err;
+        attr_done = true;
+    }
+    const size_t lds = quant_lds_bytes((int)(e - b));
+    const unsigned grid = (unsigned)cdiv(a.d_out, QROWS);
+    quant_block_kernel<<<grid, 256, lds, st>>>(a, (int)b, (int)e);
+    return hipGetLastError();
+}
+
+}  // namespace gptq
