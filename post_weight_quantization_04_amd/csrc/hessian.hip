@@ -78,6 +78,15 @@ __device__ __forceinline__ void load_slab_bf16(const uint16_t *__restrict__ X, i
     }
 }
 
+// Interior stage: every token and channel in range, no per-lane guards.
+__device__ __forceinline__ void load_slab_bf16_full(const uint16_t *__restrict__ X, int d, int64_t k, int c0,
+                                                    u32x4 (&r)[4]) {
+    const int tid = threadIdx.x;
+    const uint16_t *base = X + (k + (tid >> 5)) * (int64_t)d + c0 + (tid & 31) * 8;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = *(const u32x4 *)(base + (int64_t)(8 * p) * d);
+}
+
 __device__ __forceinline__ void store_slab_bf16(uint16_t *s, const u32x4 (&r)[4]) {
     const int tid = threadIdx.x;
 #pragma unroll
@@ -113,72 +122,78 @@ __device__ __forceinline__ void frags_bf16(const uint16_t *s, int r0, int c, bf1
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256, 1) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n,
-                                                           int d, float *__restrict__ part, int ntiles,
-                                                           int64_t tok_per_split) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BBK * BT];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BBK * BT];
+__global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n, int d,
+                                                        float *__restrict__ part, int ntiles,
+                                                        int64_t tok_per_split) {
+    // smem[buf][op]: op 0 = A slab (channels of tile row I), op 1 = B slab (tile column J)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BBK * BT];
+    constexpr int SLAB = BBK * BT;
 
     const int w = blockIdx.x;
     const int split = w / ntiles;
     int I, J;
     tile_coords(w % ntiles, I, J);
     const bool diag = (I == J);
+    const int bop = diag ? 0 : 1;          // diagonal tiles read B from the A slab
     const int64_t k0 = (int64_t)split * tok_per_split;
     const int64_t k1 = std::min<int64_t>(n, k0 + tok_per_split);
     const int nst = (k1 > k0) ? (int)((k1 - k0 + BBK - 1) / BBK) : 0;
+    const bool full_cols = (I + 1) * BT <= d;   // J <= I
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int wr = wave >> 1, wc = wave & 1;
     const int h = lane >> 5, li = lane & 31;
-    // the wave above the diagonal of a diagonal tile has nothing to compute
-    const bool active = !(diag && wr < wc);
 
     f32x16 acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
 
-    const uint16_t *Bsrc_s[2] = {diag ? sA[0] : sB[0], diag ? sA[1] : sB[1]};
     u32x4 ra[4], rb[4];
     if (nst > 0) {
         load_slab_bf16<VEC>(X, k1, d, k0, I * BT, ra);
         if (!diag) load_slab_bf16<VEC>(X, k1, d, k0, J * BT, rb);
-        store_slab_bf16(sA[0], ra);
-        if (!diag) store_slab_bf16(sB[0], rb);
+        store_slab_bf16(smem, ra);
+        if (!diag) store_slab_bf16(smem + SLAB, rb);
     }
     __syncthreads();
+    const int aoff = wr * 128 + li * 4;
+    const int boff = wc * 128 + li * 4;
     for (int st = 0; st < nst; ++st) {
         const int buf = st & 1;
         const bool more = st + 1 < nst;
         if (more) {
             const int64_t k = k0 + (int64_t)(st + 1) * BBK;
-            load_slab_bf16<VEC>(X, k1, d, k, I * BT, ra);
-            if (!diag) load_slab_bf16<VEC>(X, k1, d, k, J * BT, rb);
-        }
-        if (active) {
-            const uint16_t *a = sA[buf];
-            const uint16_t *b = Bsrc_s[buf];
-#pragma unroll
-            for (int ks = 0; ks < BBK / 16; ++ks) {
-                bf16x8 fa[4], fb[4];
-                frags_bf16(a, ks * 16 + h * 8, wr * 128 + li * 4, fa);
-                frags_bf16(b, ks * 16 + h * 8, wc * 128 + li * 4, fb);
-#pragma unroll
-                for (int ma = 0; ma < 4; ++ma)
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        acc[ma * 4 + mb] =
-                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[mb], acc[ma * 4 + mb], 0, 0, 0);
+            if (VEC && full_cols && k + BBK <= k1) {
+                load_slab_bf16_full(X, d, k, I * BT, ra);
+                if (!diag) load_slab_bf16_full(X, d, k, J * BT, rb);
+            } else {
+                load_slab_bf16<VEC>(X, k1, d, k, I * BT, ra);
+                if (!diag) load_slab_bf16<VEC>(X, k1, d, k, J * BT, rb);
             }
         }
+        const uint16_t *a = smem + (2 * buf) * SLAB;
+        const uint16_t *b = smem + (2 * buf + bop) * SLAB;
+#pragma unroll
+        for (int ks = 0; ks < BBK / 16; ++ks) {
+            bf16x8 fa[4], fb[4];
+            frags_bf16(a, ks * 16 + h * 8, aoff, fa);
+            frags_bf16(b, ks * 16 + h * 8, boff, fb);
+#pragma unroll
+            for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    acc[ma * 4 + mb] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[mb], acc[ma * 4 + mb], 0, 0, 0);
+        }
         if (more) {
-            store_slab_bf16(sA[buf ^ 1], ra);
-            if (!diag) store_slab_bf16(sB[buf ^ 1], rb);
+            store_slab_bf16(smem + (2 * (buf ^ 1)) * SLAB, ra);
+            if (!diag) store_slab_bf16(smem + (2 * (buf ^ 1) + 1) * SLAB, rb);
         }
         __syncthreads();
     }
-    if (!active) return;
+    // the wave above the diagonal of a diagonal tile computed nothing useful
+    if (diag && wr < wc) return;
     float *out = part + (int64_t)w * BT * BT;
 #pragma unroll
     for (int ma = 0; ma < 4; ++ma)
