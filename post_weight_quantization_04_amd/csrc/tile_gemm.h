@@ -1,7 +1,15 @@
 // fp32-MFMA 128x128 tile product shared by the factorization and the
-// trailing update: acc += alpha * A(128 x K) * B(K x 128), with both operands
-// given by a strided view and staged through LDS in k-major layout.
-// Four waves own 64x64 quadrants, each as 2x2 v_mfma_f32_32x32x2_f32 tiles.
+// trailing update: acc += alpha * A(128 x K) * B(K x 128).
+//
+// Operands are strided views: A(m, k) = A[m*lda + k] when A is k-contiguous,
+// else A[k*lda + m]; B(k, n) = B[k*ldb + n] when B is n-contiguous, else
+// B[n*ldb + k].  Both are staged through LDS in k-major layout ([k][m] and
+// [k][n]) in 32-deep chunks, double-buffered through registers so the next
+// chunk's global loads overlap the current chunk's MFMAs.  Interior tiles
+// with aligned rows use 16-byte loads; edges fall back to guarded scalar
+// loads.  Four waves own 64x64 quadrants, each as 2x2 v_mfma_f32_32x32x2_f32
+// tiles; accumulator layout: lane (h, li), register 4a+b <-> row 8a+4h+b,
+// column li of the 32x32 sub-tile.
 #pragma once
 #include "common.h"
 
@@ -10,16 +18,8 @@ namespace {
 
 constexpr int GT = 128;       // product tile edge
 constexpr int GK = 32;        // k chunk staged per pass
-
-struct MatRef {
-    const float *p;
-    int64_t s0, s1;           // element (a, b) at p[a*s0 + b*s1]
-    int rows, cols;           // valid range
-};
-
-__device__ __forceinline__ float mref(const MatRef &m, int a, int b) {
-    return (a < m.rows && b < m.cols) ? m.p[a * m.s0 + b * m.s1] : 0.f;
-}
+constexpr int GLD = GT + 1;   // LDS row stride (floats): transposed scalar writes stay conflict-free
+constexpr int GSTAGE = GK * GLD;
 
 __device__ __forceinline__ void tile_coords(int t, int &I, int &J) {
     int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
@@ -29,13 +29,16 @@ __device__ __forceinline__ void tile_coords(int t, int &I, int &J) {
     J = t - i * (i + 1) / 2;
 }
 
-// acc[ma*2+mb] holds the wave's 32x32 sub-tile (ma, mb) of a 128x128 tile in
-// MFMA layout: lane (h, li), register 4a+b <-> row 8a+4h+b, column li.
 __device__ __forceinline__ void tile_rc(int ma, int mb, int a, int b, int &r, int &c) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
     r = wr * 64 + ma * 32 + 8 * a + 4 * h + b;
     c = wc * 64 + mb * 32 + li;
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 }
 
 __device__ __forceinline__ void load_c(f32x16 (&acc)[4], const float *C, int64_t ldc, int rows, int cols) {
@@ -68,31 +71,110 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[4], float *C, int64_
                 }
 }
 
-// acc += alpha * A(128 x K) * B(K x 128), operands staged through LDS.
-__device__ void gemm_tile(f32x16 (&acc)[4], const MatRef &A, const MatRef &B, int K, float alpha,
-                          float (*As)[GK * GT], float (*Bs)[GK * GT]) {
+// One operand chunk: 32 (k) x 128 (m or n) values held as 16 floats per thread.
+// KCONTIG: the source is contiguous along k (element (m, k) at p[m*ld + k]).
+template <bool KCONTIG>
+struct Chunk {
+    float v[16];
+
+    // thread mapping: KCONTIG -> t%8 picks a 4-wide k quad, t/8 + 32q the row;
+    // otherwise t%32 picks a 4-wide m quad, t/32 + 8q the k row.
+    __device__ __forceinline__ void load(const float *p, int64_t ld, int kbase, int mlim, int klim, bool fast) {
+        const int t = threadIdx.x;
+        if (KCONTIG) {
+            const int kq = (t & 7) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = (t >> 3) + 32 * q;
+                const float *src = p + (int64_t)m * ld + kbase + kq;
+                if (fast) {
+                    const f32x4 x = *(const f32x4 *)src;
+                    v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[4 * q + e] = (m < mlim && kbase + kq + e < klim) ? src[e] : 0.f;
+                }
+            }
+        } else {
+            const int mq = (t & 31) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = (t >> 5) + 8 * q;
+                const float *src = p + (int64_t)(kbase + k) * ld + mq;
+                if (fast) {
+                    const f32x4 x = *(const f32x4 *)src;
+                    v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[4 * q + e] = (kbase + k < klim && mq + e < mlim) ? src[e] : 0.f;
+                }
+            }
+        }
+    }
+
+    // write into LDS stage s[k][m] (row stride GLD), scaled by alpha
+    __device__ __forceinline__ void store(float *s, float alpha) const {
+        const int t = threadIdx.x;
+        if (KCONTIG) {
+            const int kq = (t & 7) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = (t >> 3) + 32 * q;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[(kq + e) * GLD + m] = alpha * v[4 * q + e];
+            }
+        } else {
+            const int mq = (t & 31) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = (t >> 5) + 8 * q;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[k * GLD + mq + e] = alpha * v[4 * q + e];
+            }
+        }
+    }
+};
+
+// acc += alpha * A * B over K.  lds: 4 * GSTAGE floats (two stages of A and B).
+// rows/cols bound A's m and B's n; K bounds k.  vec_ok: both bases and
+// leading dimensions are 16-byte aligned (enables 16-byte loads on full chunks).
+template <bool A_KCONTIG, bool B_KCONTIG>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4], const float *A, int64_t lda, const float *B, int64_t ldb,
+                          int rows, int cols, int K, float alpha, bool vec_ok, float *lds) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
     const int nch = (K + GK - 1) / GK;
+    if (nch == 0) return;
+    const bool full_mn = rows >= GT && cols >= GT && vec_ok;
+    Chunk<A_KCONTIG> ca;
+    Chunk<B_KCONTIG> cb;
+    ca.load(A, lda, 0, rows, K, full_mn && GK <= K);
+    cb.load(B, ldb, 0, cols, K, full_mn && GK <= K);
+    ca.store(lds, alpha);
+    cb.store(lds + GSTAGE, 1.f);
+    __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
-        const int kb = ch * GK;
-#pragma unroll 4
-        for (int e = 0; e < (GK * GT) / 256; ++e) {
-            const int idx = tid + 256 * e;
-            const int kk = idx / GT, m = idx % GT;
-            As[0][idx] = alpha * mref(A, m, kb + kk);
-            Bs[0][idx] = mref(B, kb + kk, m);
+        const int buf = ch & 1;
+        const bool more = ch + 1 < nch;
+        if (more) {
+            const int kb = (ch + 1) * GK;
+            const bool fast = full_mn && kb + GK <= K;
+            ca.load(A, lda, kb, rows, K, fast);
+            cb.load(B, ldb, kb, cols, K, fast);
         }
-        __syncthreads();
+        const float *as = lds + (2 * buf) * GSTAGE;
+        const float *bs = lds + (2 * buf + 1) * GSTAGE;
 #pragma unroll
         for (int s = 0; s < GK / 2; ++s) {
             const int row = 2 * s + h;
             float fa[2], fb[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                fa[m] = As[0][row * GT + wr * 64 + m * 32 + li];
-                fb[m] = Bs[0][row * GT + wc * 64 + m * 32 + li];
+                fa[m] = as[row * GLD + wr * 64 + m * 32 + li];
+                fb[m] = bs[row * GLD + wc * 64 + m * 32 + li];
             }
 #pragma unroll
             for (int ma = 0; ma < 2; ++ma)
@@ -100,8 +182,16 @@ __device__ void gemm_tile(f32x16 (&acc)[4], const MatRef &A, const MatRef &B, in
                 for (int mb = 0; mb < 2; ++mb)
                     acc[ma * 2 + mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[ma], fb[mb], acc[ma * 2 + mb], 0, 0, 0);
         }
+        if (more) {
+            ca.store(lds + (2 * (buf ^ 1)) * GSTAGE, alpha);
+            cb.store(lds + (2 * (buf ^ 1) + 1) * GSTAGE, 1.f);
+        }
         __syncthreads();
     }
+}
+
+__device__ __forceinline__ bool aligned16(const void *p, int64_t ld) {
+    return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 4 == 0);
 }
 
 }  // namespace

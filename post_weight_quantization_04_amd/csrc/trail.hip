@@ -15,19 +15,19 @@ namespace gptq {
 namespace {
 
 __global__ __launch_bounds__(256) void trail_kernel(QuantArgs a, int b, int e) {
-    __shared__ float As[1][GK * GT];
-    __shared__ float Bs[1][GK * GT];
+    __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
     const int64_t row0 = (int64_t)blockIdx.x * GT;
     const int64_t col0 = (int64_t)e + (int64_t)blockIdx.y * GT;
     const int rows = (int)std::min<int64_t>(GT, a.d_out - row0);
     const int cols = (int)std::min<int64_t>(GT, a.d_in - col0);
     const int K = e - b;
-    MatRef A{a.E + row0, 1, a.d_out, rows, K};                     // A(m, kk) = E[kk][row0 + m]
-    MatRef B{a.U + (int64_t)b * a.d_in + col0, a.d_in, 1, K, cols};  // B(kk, n) = U[b + kk][col0 + n]
+    const float *A = a.E + row0;                                   // A(m, k) = E[k][row0 + m]
+    const float *B = a.U + (int64_t)b * a.d_in + col0;             // B(k, n) = U[b + k][col0 + n]
     float *C = a.Wp + row0 * a.d_in + col0;
     f32x16 acc[4];
     load_c(acc, C, a.d_in, rows, cols);
-    gemm_tile(acc, A, B, K, -1.f, As, Bs);
+    gemm_tile<false, false>(acc, A, a.d_out, B, a.d_in, rows, cols, K, -1.f,
+                            aligned16(A, a.d_out) && aligned16(B, a.d_in), lds);
     store_c(acc, C, a.d_in, rows, cols);
 }
 
