@@ -29,6 +29,7 @@ namespace {
 
 constexpr int BT = 256;   // bf16 tile
 constexpr int BBK = 32;   // tokens per LDS stage (bf16)
+constexpr int NBUF = 4;   // LDS ring of stages (bf16): three stages in flight while one is computed
 constexpr int FT = 128;   // fp32 tile
 constexpr int FBK = 16;   // tokens per LDS stage (fp32)
 
@@ -47,13 +48,15 @@ __device__ __forceinline__ unsigned hi_pair(unsigned a, unsigned b) {
     return (a >> 16) | (b & 0xFFFF0000u);
 }
 
-// Load one 32-token x 256-channel bf16 slab (A or B operand) into registers.
+constexpr int SLAB_PASSES = BBK / 8;   // 16-byte chunks per thread per slab
+
+// Load one BBK-token x 256-channel bf16 slab (A or B operand) into registers.
 template <bool VEC>
 __device__ __forceinline__ void load_slab_bf16(const uint16_t *__restrict__ X, int64_t n, int d,
-                                               int64_t k, int c0, u32x4 (&r)[4]) {
+                                               int64_t k, int c0, u32x4 (&r)[SLAB_PASSES]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < SLAB_PASSES; ++p) {
         const int row = (tid >> 5) + 8 * p;
         const int col = (tid & 31) * 8;
         const int64_t t = k + row;
@@ -80,17 +83,17 @@ __device__ __forceinline__ void load_slab_bf16(const uint16_t *__restrict__ X, i
 
 // Interior stage: every token and channel in range, no per-lane guards.
 __device__ __forceinline__ void load_slab_bf16_full(const uint16_t *__restrict__ X, int d, int64_t k, int c0,
-                                                    u32x4 (&r)[4]) {
+                                                    u32x4 (&r)[SLAB_PASSES]) {
     const int tid = threadIdx.x;
     const uint16_t *base = X + (k + (tid >> 5)) * (int64_t)d + c0 + (tid & 31) * 8;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) r[p] = *(const u32x4 *)(base + (int64_t)(8 * p) * d);
+    for (int p = 0; p < SLAB_PASSES; ++p) r[p] = *(const u32x4 *)(base + (int64_t)(8 * p) * d);
 }
 
-__device__ __forceinline__ void store_slab_bf16(uint16_t *s, const u32x4 (&r)[4]) {
+__device__ __forceinline__ void store_slab_bf16(uint16_t *s, const u32x4 (&r)[SLAB_PASSES]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < SLAB_PASSES; ++p) {
         const int row = (tid >> 5) + 8 * p;
         const int col = (tid & 31) * 8;
         *(u32x4 *)(s + row * BT + col) = r[p];
@@ -121,24 +124,102 @@ __device__ __forceinline__ void frags_bf16(const uint16_t *s, int r0, int c, bf1
     }
 }
 
+// p-th tile of the lower triangle in blocked order: super-tiles of 4x4 tiles
+// row by row (off-diagonal super-tiles, then the diagonal one), tiles inside
+// a super-tile row by row.
+__device__ __forceinline__ void blocked_tile(int p, int nb, int &I, int &J) {
+    constexpr int S = 4;
+    const int nsb = (nb + S - 1) / S;
+    for (int si = 0; si < nsb; ++si) {
+        const int rows = min(S, nb - S * si);
+        const int off = si * rows * S;                 // tiles in off-diagonal super-tiles of this row
+        const int dg = rows * (rows + 1) / 2;
+        if (p < off) {
+            const int sj = p / (rows * S), q = p % (rows * S);
+            I = S * si + q / S;
+            J = S * sj + q % S;
+            return;
+        }
+        p -= off;
+        if (p < dg) {
+            int r = 0;
+            while ((r + 1) * (r + 2) / 2 <= p) ++r;
+            I = S * si + r;
+            J = S * si + (p - r * (r + 1) / 2);
+            return;
+        }
+        p -= dg;
+    }
+    I = J = 0;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Interior stage, straight into LDS: each wave moves four 1 KB chunks (two
+// token rows of 256 channels each) with 16-byte global_load_lds; lane l's
+// 16 bytes land at chunk base + 16 l, i.e. the row-major slab layout.
+__device__ __forceinline__ void dma_slab_bf16(const uint16_t *__restrict__ X, int d, int64_t k, int c0, uint16_t *s) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < BBK / 8; ++q) {
+        const int chunk = wave * (BBK / 8) + q;              // 2 rows per chunk
+        const int row = 2 * chunk + (lane >> 5);
+        const uint16_t *src = X + (k + row) * (int64_t)d + c0 + (lane & 31) * 8;
+        __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(s + chunk * 512), 16, 0, 0);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Work-group barrier without the release/acquire fence of __syncthreads():
+// that fence would wait for every outstanding LDS DMA, including the stages
+// still meant to be in flight.  LDS stores of this wave are drained first;
+// DMA completion is covered by the explicit vmcnt waits before it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// wait until at most `left` of this wave's vector-memory instructions are outstanding
+__device__ __forceinline__ void wait_vm_left(int left) {
+    switch (left) {
+        case 0: wait_vm<0>(); break;
+        case 4: wait_vm<4>(); break;
+        case 8: wait_vm<8>(); break;
+        case 12: wait_vm<12>(); break;
+        case 16: wait_vm<16>(); break;
+        default: wait_vm<0>(); break;
+    }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n, int d,
-                                                        float *__restrict__ part, int ntiles,
+                                                        float *__restrict__ part, int ntiles, int nb, int nsplit,
                                                         int64_t tok_per_split) {
     // smem[buf][op]: op 0 = A slab (channels of tile row I), op 1 = B slab (tile column J)
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BBK * BT];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * BBK * BT];
     constexpr int SLAB = BBK * BT;
 
-    const int w = blockIdx.x;
-    const int split = w / ntiles;
+    // Work-group ids go round-robin over the 8 XCDs; give each XCD a contiguous
+    // run of (split, tile) units so that the groups it runs at once share a
+    // token range and, through the blocked tile order, few column blocks.
+    const int per_xcd = gridDim.x / 8;
+    const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (unit >= ntiles * nsplit) return;
+    const int split = unit / ntiles;
     int I, J;
-    tile_coords(w % ntiles, I, J);
+    blocked_tile(unit % ntiles, nb, I, J);
+    const int w = split * ntiles + I * (I + 1) / 2 + J;    // partial slot: split-major, row-major tile
     const bool diag = (I == J);
-    const int bop = diag ? 0 : 1;          // diagonal tiles read B from the A slab
+    const int bop = diag ? 0 : 1;
     const int64_t k0 = (int64_t)split * tok_per_split;
     const int64_t k1 = std::min<int64_t>(n, k0 + tok_per_split);
     const int nst = (k1 > k0) ? (int)((k1 - k0 + BBK - 1) / BBK) : 0;
-    const bool full_cols = (I + 1) * BT <= d;   // J <= I
+    const bool full_cols = VEC && (I + 1) * BT <= d;        // J <= I
+    const int per_stage = diag ? BBK / 8 : 2 * (BBK / 8);   // vector-memory instructions per stage per wave
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -149,31 +230,37 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
 
-    u32x4 ra[4], rb[4];
-    if (nst > 0) {
-        load_slab_bf16<VEC>(X, k1, d, k0, I * BT, ra);
-        if (!diag) load_slab_bf16<VEC>(X, k1, d, k0, J * BT, rb);
-        store_slab_bf16(smem, ra);
-        if (!diag) store_slab_bf16(smem + SLAB, rb);
-    }
-    __syncthreads();
+    // stage st goes to buffer st % NBUF; interior stages by DMA, edges through registers
+    auto issue = [&](int st) {
+        const int64_t k = k0 + (int64_t)st * BBK;
+        uint16_t *buf = smem + (st % NBUF) * 2 * SLAB;
+        if (full_cols && k + BBK <= k1) {
+            dma_slab_bf16(X, d, k, I * BT, buf);
+            if (!diag) dma_slab_bf16(X, d, k, J * BT, buf + SLAB);
+        } else {
+            u32x4 r[SLAB_PASSES];
+            load_slab_bf16<VEC>(X, k1, d, k, I * BT, r);
+            wait_vm<0>();
+            store_slab_bf16(buf, r);
+            if (!diag) {
+                load_slab_bf16<VEC>(X, k1, d, k, J * BT, r);
+                wait_vm<0>();
+                store_slab_bf16(buf + SLAB, r);
+            }
+        }
+    };
+    for (int st = 0; st < NBUF - 1 && st < nst; ++st) issue(st);
+
     const int aoff = wr * 128 + li * 4;
     const int boff = wc * 128 + li * 4;
     for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        const bool more = st + 1 < nst;
-        if (more) {
-            const int64_t k = k0 + (int64_t)(st + 1) * BBK;
-            if (VEC && full_cols && k + BBK <= k1) {
-                load_slab_bf16_full(X, d, k, I * BT, ra);
-                if (!diag) load_slab_bf16_full(X, d, k, J * BT, rb);
-            } else {
-                load_slab_bf16<VEC>(X, k1, d, k, I * BT, ra);
-                if (!diag) load_slab_bf16<VEC>(X, k1, d, k, J * BT, rb);
-            }
-        }
-        const uint16_t *a = smem + (2 * buf) * SLAB;
-        const uint16_t *b = smem + (2 * buf + bop) * SLAB;
+        // stage st complete for this wave: later issued stages may stay in flight
+        const int later = std::min(NBUF - 2, nst - 1 - st);
+        wait_vm_left(later * per_stage);
+        lds_barrier();
+        if (st + NBUF - 1 < nst) issue(st + NBUF - 1);       // refills the buffer computed last iteration
+        const uint16_t *a = smem + (st % NBUF) * 2 * SLAB;
+        const uint16_t *b = a + bop * SLAB;
 #pragma unroll
         for (int ks = 0; ks < BBK / 16; ++ks) {
             bf16x8 fa[4], fb[4];
@@ -186,11 +273,6 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
                     acc[ma * 4 + mb] =
                         __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[mb], acc[ma * 4 + mb], 0, 0, 0);
         }
-        if (more) {
-            store_slab_bf16(smem + (2 * (buf ^ 1)) * SLAB, ra);
-            if (!diag) store_slab_bf16(smem + (2 * (buf ^ 1) + 1) * SLAB, rb);
-        }
-        __syncthreads();
     }
     // the wave above the diagonal of a diagonal tile computed nothing useful
     if (diag && wr < wc) return;
@@ -412,10 +494,13 @@ hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t
     const int bk = is_bf16 ? BBK : FBK;
     const int64_t tok = cdiv(cdiv(n, p.s_off), bk) * bk;
     if (is_bf16) {
+        const unsigned grid = (unsigned)(cdiv(p.nwg, 8) * 8);
         if (d % 8 == 0)
-            hess_bf16_kernel<true><<<p.nwg, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, tok);
+            hess_bf16_kernel<true><<<grid, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, p.nb,
+                                                         p.s_off, tok);
         else
-            hess_bf16_kernel<false><<<p.nwg, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, tok);
+            hess_bf16_kernel<false><<<grid, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, p.nb,
+                                                          p.s_off, tok);
     } else {
         if (d % 4 == 0)
             hess_f32_kernel<true><<<p.nwg, 256, 0, st>>>((const float *)X, n, (int)d, partials, p.ntiles, tok);
