@@ -116,6 +116,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="q_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
+    ap.add_argument("--unprofiled-check", action="store_true",
+                    help="also time the steps once with stage events off and log both figures")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the quantizer runs on a single MI355X and this build has no "
@@ -124,6 +129,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
+        return
 
     import post_weight_quantization_04_amd as P
     from post_weight_quantization_04_amd import synth
@@ -158,10 +173,18 @@ def main():
         step()
         torch.cuda.synchronize()
         log(f"bench: warmup step {i + 1}/{args.warmup} done")
-    P.profile_enable(True)
-    P.profile_read(reset=True)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.unprofiled_check:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        log(f"bench: {ev0.elapsed_time(ev1) / args.steps:.3f} ms/step with stage events off")
+    P.profile_enable(True)
+    P.profile_read(reset=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)

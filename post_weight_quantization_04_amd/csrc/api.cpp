@@ -152,7 +152,7 @@ Workspace layout(const LayerShape &L, char *base) {
     w.E = (float *)take(sizeof(float) * (size_t)L.block_int * L.d_out);
     w.codes = (uint8_t *)take((size_t)d * L.d_out);
     w.panel = (float *)take(sizeof(float) * (size_t)d * gptq::FACT_NB);
-    w.dinv = (float *)take(sizeof(float) * gptq::FACT_NB * gptq::FACT_NB);
+    w.dinv = (float *)take(sizeof(float) * 2 * gptq::FACT_NB * gptq::FACT_NB);  // ping-pong pair
     w.dg = (float *)take(sizeof(float) * d);
     w.ud = (float *)take(sizeof(float) * d);
     w.uinv = (float *)take(sizeof(float) * d);

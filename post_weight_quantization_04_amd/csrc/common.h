@@ -58,6 +58,8 @@ hipError_t prep_gather_w(const void *W, int is_bf16, const int32_t *perm, int64_
 // lower triangular inverse, then the flip that yields U.
 // ---------------------------------------------------------------------------
 constexpr int FACT_NB = 128;
+// panel: d * FACT_NB floats; dinv: 2 * FACT_NB^2 floats (the inverse of the
+// current diagonal block and, written ahead by the fused update, the next one).
 hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t *info,
                          hipStream_t st);
 // U[k][j] = M[d-1-k][d-1-j] for k < j (in place, upper triangle);

@@ -9,12 +9,13 @@
 // upper triangle through LDS so that H stays bitwise symmetric.
 //
 // bf16 path: 256x256 tiles, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16.
-// X is staged through LDS as loaded (token-major rows).  MFMA operands need 8
-// consecutive tokens of one channel per lane, so each lane reads four
-// channels of one token with ds_read_b64 for eight tokens and regroups the
-// 16-bit halves in registers.  MFMA output row i of operand slot m maps to
-// channel 4*i + m, which makes the four slots of a lane land on four adjacent
-// columns (one 16-byte store).
+// X is staged through LDS as loaded (token-major rows of 512 bytes), with the
+// 16-byte units of each row XOR-swizzled by the token index.  MFMA operands
+// need 8 consecutive tokens of one channel per lane; the LDS transpose read
+// ds_read_b64_tr_b16 delivers them directly: within each 16-lane group, lane
+// i points at 4 channels of token i/4 and receives 4 tokens of one channel.
+// Two such reads form one operand, so no register regrouping is needed, and
+// the swizzle keeps each 32-lane half of a read on distinct banks.
 //
 // fp32 path: 128x128 tiles, 4 waves of 64x64, v_mfma_f32_32x32x2_f32.
 #include "common.h"
@@ -41,14 +42,11 @@ __device__ __forceinline__ void tile_coords(int t, int &I, int &J) {
     J = t - i * (i + 1) / 2;
 }
 
-__device__ __forceinline__ unsigned lo_pair(unsigned a, unsigned b) {
-    return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ unsigned hi_pair(unsigned a, unsigned b) {
-    return (a >> 16) | (b & 0xFFFF0000u);
-}
-
 constexpr int SLAB_PASSES = BBK / 8;   // 16-byte chunks per thread per slab
+
+// LDS position (in 16-byte units) of channel unit u (8 channels) of token t
+// inside a slab: row t holds 32 units, permuted by u ^ 4 (t % 4).
+__device__ __forceinline__ int slab_unit(int t, int u) { return t * 32 + (u ^ (4 * (t & 3))); }
 
 // Load one BBK-token x 256-channel bf16 slab (A or B operand) into registers.
 template <bool VEC>
@@ -81,47 +79,27 @@ __device__ __forceinline__ void load_slab_bf16(const uint16_t *__restrict__ X, i
     }
 }
 
-// Interior stage: every token and channel in range, no per-lane guards.
-__device__ __forceinline__ void load_slab_bf16_full(const uint16_t *__restrict__ X, int d, int64_t k, int c0,
-                                                    u32x4 (&r)[SLAB_PASSES]) {
-    const int tid = threadIdx.x;
-    const uint16_t *base = X + (k + (tid >> 5)) * (int64_t)d + c0 + (tid & 31) * 8;
-#pragma unroll
-    for (int p = 0; p < SLAB_PASSES; ++p) r[p] = *(const u32x4 *)(base + (int64_t)(8 * p) * d);
-}
-
 __device__ __forceinline__ void store_slab_bf16(uint16_t *s, const u32x4 (&r)[SLAB_PASSES]) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int p = 0; p < SLAB_PASSES; ++p) {
         const int row = (tid >> 5) + 8 * p;
-        const int col = (tid & 31) * 8;
-        *(u32x4 *)(s + row * BT + col) = r[p];
+        *(u32x4 *)(s + 8 * slab_unit(row, tid & 31)) = r[p];
     }
 }
 
-// Eight tokens (rows r0..r0+7) x four channels (c..c+3) -> four MFMA operands.
-__device__ __forceinline__ void frags_bf16(const uint16_t *s, int r0, int c, bf16x8 (&f)[4]) {
-    u32x2 v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = *(const u32x2 *)(s + (r0 + e) * BT + c);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        u32x4 q;
-        const int half = m >> 1;
-        if ((m & 1) == 0) {
-            q.x = lo_pair(v[0][half], v[1][half]);
-            q.y = lo_pair(v[2][half], v[3][half]);
-            q.z = lo_pair(v[4][half], v[5][half]);
-            q.w = lo_pair(v[6][half], v[7][half]);
-        } else {
-            q.x = hi_pair(v[0][half], v[1][half]);
-            q.y = hi_pair(v[2][half], v[3][half]);
-            q.z = hi_pair(v[4][half], v[5][half]);
-            q.w = hi_pair(v[6][half], v[7][half]);
-        }
-        f[m] = __builtin_bit_cast(bf16x8, q);
-    }
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One MFMA operand: tokens t0..t0+7 (k slots 0..7) of 32 channels.  off is
+// this lane's byte offset for tokens t0..t0+3; tokens t0+4..t0+7 sit four
+// rows (2 KB) further on with the same swizzle (t % 4 unchanged).
+__device__ __forceinline__ bf16x8 tr_operand(const lds_char *base, int off) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + off + 4 * 512));
+    const __attribute__((ext_vector_type(8))) short v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // p-th tile of the lower triangle in blocked order: super-tiles of 4x4 tiles
@@ -156,16 +134,18 @@ __device__ __forceinline__ void blocked_tile(int p, int nb, int &I, int &J) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Interior stage, straight into LDS: each wave moves four 1 KB chunks (two
-// token rows of 256 channels each) with 16-byte global_load_lds; lane l's
-// 16 bytes land at chunk base + 16 l, i.e. the row-major slab layout.
+// Interior stage, straight into LDS: each wave moves BBK/8 chunks of 1 KB
+// (two token rows of 256 channels each) with 16-byte global_load_lds.  Lane
+// l's 16 bytes land at chunk base + 16 l, so the lane fetches the channel
+// unit that the swizzle places there.
 __device__ __forceinline__ void dma_slab_bf16(const uint16_t *__restrict__ X, int d, int64_t k, int c0, uint16_t *s) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < BBK / 8; ++q) {
         const int chunk = wave * (BBK / 8) + q;              // 2 rows per chunk
         const int row = 2 * chunk + (lane >> 5);
-        const uint16_t *src = X + (k + row) * (int64_t)d + c0 + (lane & 31) * 8;
+        const int unit = (lane & 31) ^ (4 * (row & 3));
+        const uint16_t *src = X + (k + row) * (int64_t)d + c0 + unit * 8;
         __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(s + chunk * 512), 16, 0, 0);
     }
 }
@@ -191,6 +171,8 @@ __device__ __forceinline__ void wait_vm_left(int left) {
         case 8: wait_vm<8>(); break;
         case 12: wait_vm<12>(); break;
         case 16: wait_vm<16>(); break;
+        case 20: wait_vm<20>(); break;
+        case 24: wait_vm<24>(); break;
         default: wait_vm<0>(); break;
     }
 }
@@ -198,16 +180,21 @@ __device__ __forceinline__ void wait_vm_left(int left) {
 template <bool VEC>
 __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n, int d,
                                                         float *__restrict__ part, int ntiles, int nb, int nsplit,
-                                                        int64_t tok_per_split) {
+                                                        int64_t tok_per_split, int round_wgs) {
     // smem[buf][op]: op 0 = A slab (channels of tile row I), op 1 = B slab (tile column J)
     __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * BBK * BT];
     constexpr int SLAB = BBK * BT;
 
-    // Work-group ids go round-robin over the 8 XCDs; give each XCD a contiguous
-    // run of (split, tile) units so that the groups it runs at once share a
-    // token range and, through the blocked tile order, few column blocks.
-    const int per_xcd = gridDim.x / 8;
-    const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    // Units (split-major, blocked tile order) are handed out one round of
+    // round_wgs groups (one per CU) at a time.  Work-group ids go round-robin
+    // over the 8 XCDs; inside a round each XCD takes a contiguous run of units,
+    // so the groups it runs at once share a token range and few column blocks
+    // (reuse in its L2), while all XCDs stream the same token range together
+    // (reuse in the memory-side cache instead of one HBM read per XCD).
+    const int base = (int)(blockIdx.x / round_wgs) * round_wgs;
+    const int m = min(round_wgs, (int)gridDim.x - base);    // multiple of 8
+    const int q = (int)blockIdx.x - base;
+    const int unit = base + (m / 8) * (q % 8) + q / 8;
     if (unit >= ntiles * nsplit) return;
     const int split = unit / ntiles;
     int I, J;
@@ -251,44 +238,80 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
     };
     for (int st = 0; st < NBUF - 1 && st < nst; ++st) issue(st);
 
-    const int aoff = wr * 128 + li * 4;
-    const int boff = wc * 128 + li * 4;
-    for (int st = 0; st < nst; ++st) {
-        // stage st complete for this wave: later issued stages may stay in flight
-        const int later = std::min(NBUF - 2, nst - 1 - st);
-        wait_vm_left(later * per_stage);
-        lds_barrier();
-        if (st + NBUF - 1 < nst) issue(st + NBUF - 1);       // refills the buffer computed last iteration
-        const uint16_t *a = smem + (st % NBUF) * 2 * SLAB;
-        const uint16_t *b = a + bop * SLAB;
+    // Transpose-read addressing.  Lane l sits in 16-lane group g = l / 16 at
+    // index i = l % 16; for operand block m (32 channels at 32 m of the wave's
+    // 128) it points at token 8 (g / 2) + i / 4 of the k step and channels
+    // 16 (g % 2) + 4 (i % 4) .. +3, swizzled by the token's i / 4.
+    const int g = lane >> 4, i16 = lane & 15;
+    const int q4 = i16 >> 2;
+    const int lane_row = (8 * (g >> 1) + q4) * 512 + (i16 & 1) * 8;
+    const int lane_unit = 2 * (g & 1) + ((i16 & 3) >> 1);
+    int offa[4], offb[4];
 #pragma unroll
-        for (int ks = 0; ks < BBK / 16; ++ks) {
-            bf16x8 fa[4], fb[4];
-            frags_bf16(a, ks * 16 + h * 8, aoff, fa);
-            frags_bf16(b, ks * 16 + h * 8, boff, fb);
+    for (int m = 0; m < 4; ++m) {
+        offa[m] = lane_row + 16 * (wr * 16 + 4 * (m ^ q4) + lane_unit);
+        offb[m] = lane_row + 16 * (wc * 16 + 4 * (m ^ q4) + lane_unit) + bop * SLAB * 2;
+    }
+    const lds_char *lds = (const lds_char *)smem;
+    // operands of k step ks (16 tokens) of stage st
+    auto frags = [&](int st, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+        const lds_char *a = lds + (st % NBUF) * 2 * SLAB * 2 + ks * 16 * 512;
 #pragma unroll
-            for (int ma = 0; ma < 4; ++ma)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc[ma * 4 + mb] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[mb], acc[ma * 4 + mb], 0, 0, 0);
+        for (int m = 0; m < 4; ++m) {
+            fa[m] = tr_operand(a, offa[m]);
+            fb[m] = tr_operand(a, offb[m]);
         }
+    };
+    auto mfma16 = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+        for (int ma = 0; ma < 4; ++ma)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                acc[ma * 4 + mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ma], fb[mb], acc[ma * 4 + mb], 0, 0, 0);
+    };
+    // Software pipeline over the two k steps of a stage: the first operands
+    // of stage st+1 are read while the second half of stage st multiplies, so
+    // the wait for the next stage and the barrier sit behind queued MFMAs.
+    static_assert(BBK == 32, "two k steps per stage");
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    // Ring: stage j lives in buffer j % NBUF.  Stages 0..NBUF-2 were issued
+    // above; each barrier below is passed only once every wave has finished
+    // reading the stage before it (lds_barrier drains this wave's LDS reads),
+    // so the buffer of that stage is refilled right after the barrier.
+    if (nst > 0) {
+        wait_vm_left(std::min(NBUF - 2, nst - 1) * per_stage);   // stage 0 landed
+        lds_barrier();
+        if (NBUF - 1 < nst) issue(NBUF - 1);                      // the one buffer still free
+        frags(0, 0, fa0, fb0);
+    }
+    for (int st = 0; st < nst; ++st) {
+        frags(st, 1, fa1, fb1);
+        mfma16(fa0, fb0);
+        if (st + 1 < nst) {
+            // stage st+1 landed for this wave; stages up to st+NBUF-1 may stay in flight
+            wait_vm_left(std::min(NBUF - 2, nst - 2 - st) * per_stage);
+            lds_barrier();                                        // all reads of stage st are done
+            if (st + NBUF < nst) issue(st + NBUF);                // into the buffer of stage st
+            frags(st + 1, 0, fa0, fb0);
+        }
+        mfma16(fa1, fb1);
     }
     // the wave above the diagonal of a diagonal tile computed nothing useful
     if (diag && wr < wc) return;
+    // accumulator layout: lane (h, li), register 4a+b <-> row 8a+4h+b, column li
     float *out = part + (int64_t)w * BT * BT;
 #pragma unroll
     for (int ma = 0; ma < 4; ++ma)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int r = wr * 128 + 4 * (8 * a + 4 * h + b) + ma;
-                const int c = wc * 128 + 4 * li;
-                f32x4 v = {acc[ma * 4 + 0][4 * a + b], acc[ma * 4 + 1][4 * a + b],
-                           acc[ma * 4 + 2][4 * a + b], acc[ma * 4 + 3][4 * a + b]};
-                *(f32x4 *)(out + r * BT + c) = v;
-            }
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int r = wr * 128 + 32 * ma + 8 * a + 4 * h + b;
+                    const int c = wc * 128 + 32 * mb + li;
+                    out[r * BT + c] = acc[ma * 4 + mb][4 * a + b];
+                }
 }
 
 template <bool VEC>
@@ -490,17 +513,17 @@ size_t hessian_ws_bytes(const HessPlan &p) {
 hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t d, float *partials,
                                   const HessPlan &p, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    (void)cu_count;
+    const int round_wgs = std::max(8, cu_count() / 8 * 8);   // grid and rounds stay multiples of 8
     const int bk = is_bf16 ? BBK : FBK;
     const int64_t tok = cdiv(cdiv(n, p.s_off), bk) * bk;
     if (is_bf16) {
         const unsigned grid = (unsigned)(cdiv(p.nwg, 8) * 8);
         if (d % 8 == 0)
             hess_bf16_kernel<true><<<grid, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, p.nb,
-                                                         p.s_off, tok);
+                                                         p.s_off, tok, round_wgs);
         else
             hess_bf16_kernel<false><<<grid, 256, 0, st>>>((const uint16_t *)X, n, (int)d, partials, p.ntiles, p.nb,
-                                                          p.s_off, tok);
+                                                          p.s_off, tok, round_wgs);
     } else {
         if (d % 4 == 0)
             hess_f32_kernel<true><<<p.nwg, 256, 0, st>>>((const float *)X, n, (int)d, partials, p.ntiles, tok);
