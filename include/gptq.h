@@ -74,7 +74,7 @@ typedef enum {
  *            x_dtype) bytes (may be NULL when that size is 0).
  * n == 0 is a no-op.  Calling it on consecutive token chunks equals one call
  * on their concatenation up to fp32 rounding; results are deterministic.
- * Errors: EINVAL (null pointer, n < 0, d_in < 1, bad dtype), ENOMEM
+ * Errors: EINVAL (null pointer, n < 0, d_in outside [1, 2^20], bad dtype), ENOMEM
  * (workspace too small), EHIP.
  * ------------------------------------------------------------------------- */
 GPTQ_API size_t gptq_hessian_workspace_size(int64_t n, int64_t d_in, gptq_dtype x_dtype);

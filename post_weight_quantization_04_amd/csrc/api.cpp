@@ -256,7 +256,7 @@ int64_t gptq_num_groups(int64_t d_in, int group_size) {
 }
 
 size_t gptq_hessian_workspace_size(int64_t n, int64_t d_in, gptq_dtype x_dtype) {
-    if (n < 0 || d_in < 1 || (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16)) return 0;
+    if (n < 0 || d_in < 1 || d_in > (int64_t)1 << 20 || (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16)) return 0;
     if (n == 0) return 0;
     return gptq::hessian_ws_bytes(gptq::hessian_plan(n, d_in, x_dtype == GPTQ_BF16));
 }
@@ -266,7 +266,7 @@ gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, int64_t n
     g_err.clear();
     if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "x_dtype must be GPTQ_F32 or GPTQ_BF16");
     if (n < 0) return fail(GPTQ_EINVAL, "n must be >= 0");
-    if (d_in < 1 || d_in > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "d_in must be >= 1");
+    if (d_in < 1 || d_in > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d_in must be in [1, 2^20]");
     if (!H) return fail(GPTQ_EINVAL, "H is NULL");
     if (n == 0) return GPTQ_OK;
     if (!X) return fail(GPTQ_EINVAL, "X is NULL");

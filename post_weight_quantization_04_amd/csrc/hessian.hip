@@ -132,23 +132,6 @@ __device__ __forceinline__ void blocked_tile(int p, int nb, int &I, int &J) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-// Interior stage, straight into LDS: each wave moves BBK/8 chunks of 1 KB
-// (two token rows of 256 channels each) with 16-byte global_load_lds.  Lane
-// l's 16 bytes land at chunk base + 16 l, so the lane fetches the channel
-// unit that the swizzle places there.
-__device__ __forceinline__ void dma_slab_bf16(const uint16_t *__restrict__ X, int d, int64_t k, int c0, uint16_t *s) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < BBK / 8; ++q) {
-        const int chunk = wave * (BBK / 8) + q;              // 2 rows per chunk
-        const int row = 2 * chunk + (lane >> 5);
-        const int unit = (lane & 31) ^ (4 * (row & 3));
-        const uint16_t *src = X + (k + row) * (int64_t)d + c0 + unit * 8;
-        __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(s + chunk * 512), 16, 0, 0);
-    }
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -177,38 +160,45 @@ __device__ __forceinline__ void wait_vm_left(int left) {
     }
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n, int d,
-                                                        float *__restrict__ part, int ntiles, int nb, int nsplit,
-                                                        int64_t tok_per_split, int round_wgs) {
-    // smem[buf][op]: op 0 = A slab (channels of tile row I), op 1 = B slab (tile column J)
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * BBK * BT];
+// Instruction order for the second half of a stage: the next stage's first
+// operand reads go out between the first MFMAs, then one refill DMA per one
+// or two MFMAs, so that a DMA waiting for queue space never holds back a long
+// run of MFMAs.  (The reads must precede the DMAs: LDS aliasing is unknown to
+// the compiler.)
+template <int NDMA>
+__device__ __forceinline__ void interleave_refill() {
+    constexpr int MFMA = 0x008, VMEM = 0x010, DSR = 0x100;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(DSR, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(MFMA, 8 / NDMA, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+}
+
+// One (split, tile) unit over tokens [k0, k1).  DIAG: I == J, only the A slab
+// is staged and the B operands read it too.
+//
+// VEC (d % 8 == 0): every stage is moved by 16-byte buffer loads straight into
+// LDS through a buffer resource that spans exactly this unit's token rows, so
+// rows at or past k1 (the ragged last stage, and the stages issued past the
+// end to keep the ring uniform) arrive as zeros without a branch.  Channels
+// past d inside a row only feed partial-tile rows and columns past d, which
+// the reduction never reads.  Otherwise every stage goes through registers
+// with per-element guards.
+template <bool VEC, bool DIAG>
+__device__ __forceinline__ void bf16_unit(const uint16_t *__restrict__ X, int64_t d, int I, int J, int64_t k0,
+                                          int64_t k1, float *__restrict__ out, uint16_t *smem) {
     constexpr int SLAB = BBK * BT;
-
-    // Units (split-major, blocked tile order) are handed out one round of
-    // round_wgs groups (one per CU) at a time.  Work-group ids go round-robin
-    // over the 8 XCDs; inside a round each XCD takes a contiguous run of units,
-    // so the groups it runs at once share a token range and few column blocks
-    // (reuse in its L2), while all XCDs stream the same token range together
-    // (reuse in the memory-side cache instead of one HBM read per XCD).
-    const int base = (int)(blockIdx.x / round_wgs) * round_wgs;
-    const int m = min(round_wgs, (int)gridDim.x - base);    // multiple of 8
-    const int q = (int)blockIdx.x - base;
-    const int unit = base + (m / 8) * (q % 8) + q / 8;
-    if (unit >= ntiles * nsplit) return;
-    const int split = unit / ntiles;
-    int I, J;
-    blocked_tile(unit % ntiles, nb, I, J);
-    const int w = split * ntiles + I * (I + 1) / 2 + J;    // partial slot: split-major, row-major tile
-    const bool diag = (I == J);
-    const int bop = diag ? 0 : 1;
-    const int64_t k0 = (int64_t)split * tok_per_split;
-    const int64_t k1 = std::min<int64_t>(n, k0 + tok_per_split);
+    constexpr int per_stage = (DIAG ? 1 : 2) * (BBK / 8);   // vector-memory instructions per stage per wave
     const int nst = (k1 > k0) ? (int)((k1 - k0 + BBK - 1) / BBK) : 0;
-    const bool full_cols = VEC && (I + 1) * BT <= d;        // J <= I
-    const int per_stage = diag ? BBK / 8 : 2 * (BBK / 8);   // vector-memory instructions per stage per wave
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS DMA bases go to M0
     const int lane = threadIdx.x & 63;
     const int wr = wave >> 1, wc = wave & 1;
     const int h = lane >> 5, li = lane & 31;
@@ -217,26 +207,61 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
 
-    // stage st goes to buffer st % NBUF; interior stages by DMA, edges through registers
-    auto issue = [&](int st) {
-        const int64_t k = k0 + (int64_t)st * BBK;
-        uint16_t *buf = smem + (st % NBUF) * 2 * SLAB;
-        if (full_cols && k + BBK <= k1) {
-            dma_slab_bf16(X, d, k, I * BT, buf);
-            if (!diag) dma_slab_bf16(X, d, k, J * BT, buf + SLAB);
-        } else {
-            u32x4 r[SLAB_PASSES];
-            load_slab_bf16<VEC>(X, k1, d, k, I * BT, r);
-            wait_vm<0>();
-            store_slab_bf16(buf, r);
-            if (!diag) {
-                load_slab_bf16<VEC>(X, k1, d, k, J * BT, r);
-                wait_vm<0>();
-                store_slab_bf16(buf + SLAB, r);
-            }
+    // DMA addressing: wave chunk q covers token rows 2 (wave * BBK/8 + q) and
+    // +1 of a stage; lane l's 16 bytes land at chunk base + 16 l and hold the
+    // channel unit that the swizzle places there.
+    // base and size go through readfirstlane so the descriptor lives in SGPRs
+    const uint64_t xbase = reinterpret_cast<uint64_t>(X + k0 * d);
+    // (readfirstlane returns int: widen through uint32_t, never sign-extend)
+    const uint64_t xb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(xbase >> 32)) << 32) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)xbase);
+    const int nrec = __builtin_amdgcn_readfirstlane((int)(std::max<int64_t>(k1 - k0, 0) * d * 2));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)xb, (short)0, nrec, 0x00020000);
+    int dma_off[BBK / 8];
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < BBK / 8; ++q) {
+            const int row = 2 * (wave * (BBK / 8) + q) + (lane >> 5);
+            const int unit = (lane & 31) ^ (4 * (row & 3));
+            dma_off[q] = (int)((row * d + unit * 8) * 2);
+        }
+    }
+    auto dma = [&](int st) {
+        const int stage_off = (int)((int64_t)st * BBK * d * 2);
+        lds_void_t *buf = (lds_void_t *)(smem + (st % NBUF) * 2 * SLAB);
+#pragma unroll
+        for (int q = 0; q < BBK / 8; ++q) {
+            const int chunk = wave * (BBK / 8) + q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)((lds_char *)buf + chunk * 1024), 16,
+                                                     dma_off[q] + stage_off + I * BT * 2, 0, 0, 0);
+            if (!DIAG)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)((lds_char *)buf + SLAB * 2 + chunk * 1024),
+                                                         16, dma_off[q] + stage_off + J * BT * 2, 0, 0, 0);
         }
     };
-    for (int st = 0; st < NBUF - 1 && st < nst; ++st) issue(st);
+    auto reg_issue = [&](int st) {
+        if (st >= nst) return;
+        const int64_t k = k0 + (int64_t)st * BBK;
+        uint16_t *buf = smem + (st % NBUF) * 2 * SLAB;
+        u32x4 r[SLAB_PASSES];
+        load_slab_bf16<VEC>(X, k1, (int)d, k, I * BT, r);
+        wait_vm<0>();
+        store_slab_bf16(buf, r);
+        if (!DIAG) {
+            load_slab_bf16<VEC>(X, k1, (int)d, k, J * BT, r);
+            wait_vm<0>();
+            store_slab_bf16(buf + SLAB, r);
+        }
+    };
+    auto issue = [&](int st) {
+        if (VEC)
+            dma(st);
+        else
+            reg_issue(st);
+    };
+    if (nst > 0) {
+        for (int st = 0; st < NBUF - 1; ++st) issue(st);
+    }
 
     // Transpose-read addressing.  Lane l sits in 16-lane group g = l / 16 at
     // index i = l % 16; for operand block m (32 channels at 32 m of the wave's
@@ -250,7 +275,7 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         offa[m] = lane_row + 16 * (wr * 16 + 4 * (m ^ q4) + lane_unit);
-        offb[m] = lane_row + 16 * (wc * 16 + 4 * (m ^ q4) + lane_unit) + bop * SLAB * 2;
+        offb[m] = lane_row + 16 * (wc * 16 + 4 * (m ^ q4) + lane_unit) + (DIAG ? 0 : SLAB * 2);
     }
     const lds_char *lds = (const lds_char *)smem;
     // operands of k step ks (16 tokens) of stage st
@@ -272,34 +297,40 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
     // Software pipeline over the two k steps of a stage: the first operands
     // of stage st+1 are read while the second half of stage st multiplies, so
     // the wait for the next stage and the barrier sit behind queued MFMAs.
+    // Ring: stage j lives in buffer j % NBUF, and NBUF-2 stages beyond the
+    // one waited for are always in flight (past the end they load zeros).
+    // Each barrier is passed only once every wave has finished reading the
+    // stage before it (lds_barrier drains this wave's LDS reads), so that
+    // stage's buffer is refilled right after the barrier.
     static_assert(BBK == 32, "two k steps per stage");
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    // Ring: stage j lives in buffer j % NBUF.  Stages 0..NBUF-2 were issued
-    // above; each barrier below is passed only once every wave has finished
-    // reading the stage before it (lds_barrier drains this wave's LDS reads),
-    // so the buffer of that stage is refilled right after the barrier.
     if (nst > 0) {
-        wait_vm_left(std::min(NBUF - 2, nst - 1) * per_stage);   // stage 0 landed
+        wait_vm_left((NBUF - 2) * per_stage);                   // stage 0 landed
         lds_barrier();
-        if (NBUF - 1 < nst) issue(NBUF - 1);                      // the one buffer still free
+        issue(NBUF - 1);                                         // the one buffer still free
         frags(0, 0, fa0, fb0);
-    }
-    for (int st = 0; st < nst; ++st) {
-        frags(st, 1, fa1, fb1);
-        mfma16(fa0, fb0);
-        if (st + 1 < nst) {
-            // stage st+1 landed for this wave; stages up to st+NBUF-1 may stay in flight
-            wait_vm_left(std::min(NBUF - 2, nst - 2 - st) * per_stage);
-            lds_barrier();                                        // all reads of stage st are done
-            if (st + NBUF < nst) issue(st + NBUF);                // into the buffer of stage st
+        for (int st = 0; st < nst - 1; ++st) {
+            frags(st, 1, fa1, fb1);
+            mfma16(fa0, fb0);
+            // keep the first half's MFMAs ahead of the wait and the barrier
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_left((NBUF - 2) * per_stage);               // stage st+1 landed
+            lds_barrier();                                       // all reads of stage st are done
+            __builtin_amdgcn_sched_barrier(0);
             frags(st + 1, 0, fa0, fb0);
+            issue(st + NBUF);                                    // into the buffer of stage st
+            mfma16(fa1, fb1);
+            if (VEC) interleave_refill<per_stage>();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        frags(nst - 1, 1, fa1, fb1);
+        mfma16(fa0, fb0);
         mfma16(fa1, fb1);
+        wait_vm<0>();   // stages issued past the end must land before the group's LDS is released
     }
     // the wave above the diagonal of a diagonal tile computed nothing useful
-    if (diag && wr < wc) return;
+    if (DIAG && wr < wc) return;
     // accumulator layout: lane (h, li), register 4a+b <-> row 8a+4h+b, column li
-    float *out = part + (int64_t)w * BT * BT;
 #pragma unroll
     for (int ma = 0; ma < 4; ++ma)
 #pragma unroll
@@ -312,6 +343,37 @@ __global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restri
                     const int c = wc * 128 + 32 * mb + li;
                     out[r * BT + c] = acc[ma * 4 + mb][4 * a + b];
                 }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void hess_bf16_kernel(const uint16_t *__restrict__ X, int64_t n, int d,
+                                                        float *__restrict__ part, int ntiles, int nb, int nsplit,
+                                                        int64_t tok_per_split, int round_wgs) {
+    // smem[buf][op]: op 0 = A slab (channels of tile row I), op 1 = B slab (tile column J)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * BBK * BT];
+
+    // Units (split-major, blocked tile order) are handed out one round of
+    // round_wgs groups (one per CU) at a time.  Work-group ids go round-robin
+    // over the 8 XCDs; inside a round each XCD takes a contiguous run of units,
+    // so the groups it runs at once share a token range and few column blocks
+    // (reuse in its L2), while all XCDs stream the same token range together
+    // (reuse in the memory-side cache instead of one HBM read per XCD).
+    const int base = (int)(blockIdx.x / round_wgs) * round_wgs;
+    const int m = min(round_wgs, (int)gridDim.x - base);    // multiple of 8
+    const int q = (int)blockIdx.x - base;
+    const int unit = base + (m / 8) * (q % 8) + q / 8;
+    if (unit >= ntiles * nsplit) return;
+    const int split = unit / ntiles;
+    int I, J;
+    blocked_tile(unit % ntiles, nb, I, J);
+    const int w = split * ntiles + I * (I + 1) / 2 + J;    // partial slot: split-major, row-major tile
+    const int64_t k0 = (int64_t)split * tok_per_split;
+    const int64_t k1 = std::min<int64_t>(n, k0 + tok_per_split);
+    float *out = part + (int64_t)w * BT * BT;
+    if (I == J)
+        bf16_unit<VEC, true>(X, d, I, J, k0, k1, out, smem);
+    else
+        bf16_unit<VEC, false>(X, d, I, J, k0, k1, out, smem);
 }
 
 template <bool VEC>
@@ -489,9 +551,14 @@ HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16) {
     int best_s = 1;
     double best = 1e300;
     const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(32, cdiv(std::max<int64_t>(n, 1), 4 * bk)));
-    for (int s = 1; s <= smax; ++s) {
+    // bf16 units address their token rows with 32-bit byte offsets from the
+    // unit's first row, including the ring stages issued past the end
+    const int64_t tok_limit = is_bf16 ? ((int64_t)1 << 31) / (2 * std::max<int64_t>(d, 1)) - (NBUF + 1) * BBK
+                                      : INT64_MAX;
+    for (int s = 1; s <= std::max(smax, 1); ++s) {
         const int64_t nwg = (int64_t)s * p.ntiles;
         const int64_t tok = cdiv(cdiv(std::max<int64_t>(n, 1), s), bk) * bk;
+        if (tok > tok_limit) continue;
         const double rounds = (double)cdiv(nwg, cus);
         const double bytes = 2.0 * (double)nwg * p.tile * p.tile * 4.0;
         const double t = rounds * tok * t_tok + bytes / bw;
@@ -499,6 +566,10 @@ HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16) {
             best = t;
             best_s = s;
         }
+    }
+    if (best >= 1e300) {   // token range too long for the split cap: split further
+        best_s = (int)cdiv(std::max<int64_t>(n, 1), std::max<int64_t>(tok_limit / bk * bk, bk));
+        while (cdiv(cdiv(std::max<int64_t>(n, 1), best_s), bk) * bk > tok_limit) ++best_s;
     }
     p.s_off = p.s_diag = best_s;
     p.nwg = best_s * p.ntiles;
