@@ -113,8 +113,8 @@ GPTQ_API gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, 
  *   Dequantization: W_hat[r][perm[k]] = scales[k/g][r] * (code(r,k) - zeros[k/g][r]).
  * workspace   device scratch of at least gptq_quantize_layer_workspace_size(...)
  *             bytes.
- * The call synchronizes `stream` once, after the factorization, to read the
- * positive-definiteness flag; everything after it is enqueued asynchronously.
+ * Everything is enqueued on `stream`; the call then synchronizes `stream` once,
+ * at the end, to read the factorization's positive-definiteness flag.
  * Errors: EINVAL, ENOMEM (nothing launched); ENOTSPD (outputs undefined);
  * EHIP.
  * ------------------------------------------------------------------------- */
@@ -134,7 +134,7 @@ GPTQ_API gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int6
  * the upper Cholesky factor of (H[perm][:,perm] + lambda I)^-1, i.e.
  * H_d^-1 = U^T U; entries below the diagonal are set to 0.  Uses the same
  * workspace as gptq_quantize_layer (size query with d_out = 1).  Synchronizes
- * `stream` once.  Errors as for gptq_quantize_layer.
+ * `stream` once, at the end.  Errors as for gptq_quantize_layer.
  * ------------------------------------------------------------------------- */
 GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float damp, int act_order,
                                 int32_t *perm, float *U, void *workspace, size_t workspace_bytes,

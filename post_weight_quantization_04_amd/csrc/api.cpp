@@ -177,6 +177,14 @@ gptq_status run_factor(const float *H, int64_t d, float damp, int act_order, int
         StageTimer t(3, st);
         HIPCHECK(gptq::factor_launch(w.R, d, w.panel, w.dinv, w.info, st));
     }
+    return GPTQ_OK;
+}
+
+// The factorization's pivot flag, read once everything has been enqueued so
+// that the device never idles waiting for the host in the middle of a layer.
+// On a bad pivot the later stages ran on non-finite values; they index no
+// memory by data, so they finish normally and their outputs are discarded.
+gptq_status read_pivot_flag(const Workspace &w, hipStream_t st) {
     int32_t info = 0;
     HIPCHECK(hipMemcpyAsync(&info, w.info, sizeof(int32_t), hipMemcpyDeviceToHost, st));
     HIPCHECK(hipStreamSynchronize(st));
@@ -352,7 +360,7 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
         StageTimer t(7, st);
         HIPCHECK(gptq::pack_launch(w.codes, d_out, d_in, bits, Qpacked, st));
     }
-    return GPTQ_OK;
+    return read_pivot_flag(w, st);
 }
 
 gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float damp, int act_order, int32_t *perm, float *U,
@@ -373,7 +381,7 @@ gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float damp, int ac
     if (s != GPTQ_OK) return s;
     HIPCHECK(gptq::factor_flip(w.R, d_in, w.ud, w.uinv, 1, st));
     HIPCHECK(hipMemcpyAsync(U, w.R, sizeof(float) * (size_t)d_in * d_in, hipMemcpyDeviceToDevice, st));
-    return GPTQ_OK;
+    return read_pivot_flag(w, st);
 }
 
 }  // extern "C"

@@ -39,135 +39,222 @@ namespace {
 constexpr int NB = FACT_NB;   // 128
 
 // ---------------------------------------------------------------------------
-// Diagonal block: X = chol(A)^-1 by an in-place Gauss-Jordan sweep.
-// Thread (ty, tx) = (tid%16, tid/16) keeps the 8x8 tile of rows 8ty.., cols
-// 8tx.. in registers, so a wave owns four whole tile columns.  At column j
-// the tile holds L^-1 for rows/cols <= j (the finished part) and the
-// trailing Cholesky matrix beyond.  Column j becomes l_ij = a_ij / l_jj; the
-// vector v[i] = l_ij (i > j), X[j][i] (i < j), 0 (i = j) is broadcast through
-// LDS and every element with row i > j takes T[i][c] -= l_ij * v[c]: the
-// Cholesky update for c > j and the inverse update for c < j in one pass;
-// column j itself becomes -l_ij / l_jj.
-// Latency choices: every thread tracks the eight pivots of the current tile
-// column with the same fused multiply-add the owning thread applies, so all
-// threads derive bitwise-identical pivots without a broadcast; only the wave
-// owning tile column j computes column j; row j of the inverse is published
-// unscaled at the end of the previous column and scaled by 1/l_jj on read.
-// One barrier per column (double-buffered v) plus one per tile column.
-// Rows/cols beyond kb are padded with the identity.
+// Diagonal block: X = chol(A)^-1 for one 128x128 block, by the same blocked
+// right-looking scheme as the whole factorization, on 32-wide sub-blocks and
+// entirely in LDS (matrix F, row stride FLD).  For sub-block b (rows/cols
+// [32b, 32b+32)):
+//   1. one wave: X_bb = chol(A_bb)^-1 in place (potrf32);
+//   2. panel  : P_i = A_ib X_bb^T for i > b, kept transposed in the unused
+//               upper block (b, i);  inverse rows: M_bj = -X_bb S_bj, j < b;
+//   3. update : A_ic -= P_i P_c^T (b < c <= i);  S_ij += P_i M_bj (j < b);
+//               S_ib = P_i X_bb,
+// with S_ij = sum_{m=j}^{i-1} L_im M_mj held in the consumed lower blocks.
+// Block products are 32x32x32 on v_mfma_f32_32x32x2_f32, one per wave.
+// Rows/cols at or past kb hold the identity.
 // ---------------------------------------------------------------------------
-template <int JJ>
-__device__ __forceinline__ void potrf_publish_row(const float (&T)[8][8], int ty, int tx, int jt, float *vb) {
-    // row j = 8*jt + JJ of the inverse (columns < j), unscaled
-    if (ty == jt) {
-        if (tx < jt) {
-            *(f32x4 *)(vb + 8 * tx) = f32x4{T[JJ][0], T[JJ][1], T[JJ][2], T[JJ][3]};
-            *(f32x4 *)(vb + 8 * tx + 4) = f32x4{T[JJ][4], T[JJ][5], T[JJ][6], T[JJ][7]};
-        } else if (tx == jt) {
+constexpr int FLD = NB + 1;   // LDS row stride of the 128x128 block (floats)
+static_assert(NB * FLD <= 4 * GSTAGE, "the diagonal block reuses the tile-product staging area");
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// X = chol(A)^-1 of the 32x32 block at (s, s) of F, by one wave.  Lane c
+// (both halves hold the same column) keeps column c of the working matrix in
+// registers: the trailing Cholesky matrix (both triangles, so that row j can
+// stand in for column j) and, left of the current column, the finished rows
+// of the inverse.  Step j: pivot p = T_jj, il = 1/sqrt(p); row j values
+// r_i = T_ji (i > j) come from lane i by readlane; every column c != j takes
+// T_ic -= r_i (T_jc / p) for i > j, which is the Cholesky update for c > j
+// and the inverse update for c < j; row j of the inverse is finished as
+// T_jc * il (c < j); column j becomes il on the diagonal and -T_ij / p below.
+__device__ __forceinline__ void potrf32(float *F, int s, int kb, int info_base, int32_t *__restrict__ info) {
+    // the lane's column, opaque to the optimizer: otherwise the 64 per-step
+    // lane masks (c == j, c < j) are hoisted out of the caller's loop and
+    // spill the scalar registers
+    int c;
+    asm volatile("v_and_b32 %0, 31, %1" : "=v"(c) : "v"((int)threadIdx.x));
+    float T[32];
 #pragma unroll
-            for (int c = 0; c < JJ; ++c) vb[8 * tx + c] = T[JJ][c];
+    for (int i = 0; i < 32; ++i) T[i] = (i >= c) ? F[(s + i) * FLD + s + c] : F[(s + c) * FLD + s + i];
+    int bad = 0;   // first non-positive (or NaN) pivot of this block, 1-based
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        // one step at a time: hoisting the row broadcasts of later steps only
+        // runs the scalar registers out
+        __builtin_amdgcn_sched_barrier(0);
+        const float p = readlane_f(T[j], j);
+        bad = (bad == 0 && !(p > 0.f) && s + j < kb) ? j + 1 : bad;
+        // 1/l_jj from the hardware reciprocal square root (about 1 ulp)
+        const float il = __builtin_amdgcn_rsqf(p);
+        const float il2 = il * il;
+        const float tj = T[j];
+        const bool me = (c == j);
+        const float w = me ? il2 : tj * il2;
+#pragma unroll
+        for (int i = j + 1; i < 32; ++i) {
+            const float r = readlane_f(T[j], i);
+            T[i] = fmaf(-r, w, me ? 0.f : T[i]);
+            if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // at most 8 broadcasts in flight
         }
+        T[j] = me ? il : ((c < j) ? tj * il : tj);
+    }
+    if (threadIdx.x == 0 && bad != 0 && info[0] == 0) info[0] = info_base + s + bad;
+    if (threadIdx.x < 32) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) F[(s + i) * FLD + s + c] = (i >= c) ? T[i] : 0.f;
     }
 }
 
-template <int JJ>
-__device__ __forceinline__ void potrf_step(float (&T)[8][8], float (&d8)[8], int ty, int tx, int jt, int tid, int kb,
-                                           int info_base, int32_t *__restrict__ info, float *vbuf) {
-    const int j = 8 * jt + JJ;
-    float *vb = vbuf + (JJ & 1) * NB;
-    const float p = d8[JJ];
-    if (tid == 0 && !(p > 0.f) && j < kb && info[0] == 0) info[0] = info_base + j + 1;
-    // 1/l_jj from the hardware reciprocal square root (about 1 ulp)
-    const float il = __builtin_amdgcn_rsqf(p);
-    if (tx == jt) {
-        // column j: l_ij for rows below, the inverse's column j in place
+// acc (+)= sum_k A(m, k) B(k, n) over k < 32 for one 32x32 block; A(m, k) =
+// F[a0 + m*am + k*ak], B(k, n) = F[b0 + k*bk + n*bn].  Accumulator layout:
+// lane (h, li), register 4a+b <-> row 8a+4h+b, column li.
+__device__ __forceinline__ void blk_mfma(f32x16 &acc, const float *F, int a0, int am, int ak, int b0, int bk, int bn) {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, li = lane & 31;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int i = 8 * ty + r;
-            const float lij = T[r][JJ] * il;
-            T[r][JJ] = (i > j) ? -lij * il : ((i == j) ? il : T[r][JJ]);
-            if (i >= j) vb[i] = (i > j) ? lij : 0.f;
+    for (int k = 0; k < 32; k += 2) {
+        const float av = F[a0 + li * am + (k + h) * ak];
+        const float bv = F[b0 + (k + h) * bk + li * bn];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void blk_load(f32x16 &acc, const float *F, int r0, int c0) {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, li = lane & 31;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[4 * a + b] = F[(r0 + 8 * a + 4 * h + b) * FLD + c0 + li];
+}
+
+// C = scale * acc, stored as block (r0, c0); transposed: element (m, n) goes to (r0 + n, c0 + m)
+__device__ __forceinline__ void blk_store(const f32x16 &acc, float *F, int r0, int c0, float scale, bool transposed) {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, li = lane & 31;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = 8 * a + 4 * h + b;
+            if (transposed)
+                F[(r0 + li) * FLD + c0 + m] = scale * acc[4 * a + b];
+            else
+                F[(r0 + m) * FLD + c0 + li] = scale * acc[4 * a + b];
         }
-    }
-    if (ty == jt && tx <= jt) {
-        // row j of the inverse takes its 1/l_jj (it was published unscaled)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) T[JJ][c] = (8 * tx + c < j) ? T[JJ][c] * il : T[JJ][c];
-    }
-    __syncthreads();
-    const f32x4 r0 = *(const f32x4 *)(vb + 8 * ty), r1 = *(const f32x4 *)(vb + 8 * ty + 4);
-    const f32x4 c0 = *(const f32x4 *)(vb + 8 * tx), c1 = *(const f32x4 *)(vb + 8 * tx + 4);
-    const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    float lr[8], vc[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) lr[r] = (8 * ty + r > j) ? rv[r] : 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vc[c] = (8 * tx + c < j) ? cv[c] * il : cv[c];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) T[r][c] = fmaf(-lr[r], vc[c], T[r][c]);
-    // the remaining pivots of this tile column take the same update
-#pragma unroll
-    for (int q = JJ + 1; q < 8; ++q) {
-        const float lq = vb[8 * jt + q];
-        d8[q] = fmaf(-lq, lq, d8[q]);
-    }
-    // publish row j+1 of the inverse for the next column (other buffer)
-    float *vn = vbuf + ((JJ + 1) & 1) * NB;
-    if (JJ < 7) potrf_publish_row<(JJ + 1) & 7>(T, ty, tx, jt, vn);
-    else potrf_publish_row<0>(T, ty, tx, jt + 1, vn);
 }
 
-template <int... S>
-__device__ __forceinline__ void potrf_tile_column(float (&T)[8][8], float (&d8)[8], int ty, int tx, int jt, int tid,
-                                                  int kb, int info_base, int32_t *__restrict__ info, float *vbuf,
-                                                  std::integer_sequence<int, S...>) {
-    (potrf_step<S>(T, d8, ty, tx, jt, tid, kb, info_base, info, vbuf), ...);
-}
-
-__device__ __forceinline__ void potrf_block(const float *__restrict__ src, int64_t ld, int kb, int info_base,
-                                            float *__restrict__ dinv, int32_t *__restrict__ info, float *vbuf,
-                                            float *dgbuf) {
+// F = the kb x kb block at src (row stride ld; lower triangle read), identity
+// past kb.  Loads are issued in batches so that many are in flight per thread.
+__device__ __forceinline__ void potrf_block_load(const float *__restrict__ src, int64_t ld, int kb, float *F) {
     const int tid = threadIdx.x;
-    const int ty = tid & 15, tx = tid >> 4;
-    float T[8][8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int half = 0; half < 2; ++half) {
+        float v[32];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = 8 * ty + r, cc = 8 * tx + c;
-            float v = (i == cc) ? 1.f : 0.f;
-            if (i < kb && cc < kb && cc <= i) v = src[(int64_t)i * ld + cc];
-            T[r][c] = v;
+        for (int q = 0; q < 32; ++q) {
+            const int idx = tid + 256 * (32 * half + q);
+            const int i = idx >> 7, c = idx & (NB - 1);
+            v[q] = (i < kb && c < kb && c <= i) ? src[(int64_t)i * ld + c] : (i == c ? 1.f : 0.f);
         }
-    for (int jt = 0; jt < 16; ++jt) {
-        // pivots of tile column jt: the diagonal of tile (jt, jt), current
-        if (ty == jt && tx == jt) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) dgbuf[q] = T[q][q];
+        for (int q = 0; q < 32; ++q) {
+            const int idx = tid + 256 * (32 * half + q);
+            F[(idx >> 7) * FLD + (idx & (NB - 1))] = v[q];
+        }
+    }
+}
+
+// dinv = the lower triangle of F restricted to kb x kb, zero elsewhere
+__device__ __forceinline__ void potrf_block_store(const float *F, int kb, float *__restrict__ dinv) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int idx = tid + 256 * (32 * half + q);
+            const int i = idx >> 7, c = idx & (NB - 1);
+            v[q] = (i < kb && c < kb && c <= i) ? F[i * FLD + c] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 32; ++q) dinv[tid + 256 * (32 * half + q)] = v[q];
+    }
+}
+
+// F (NB x FLD floats in LDS, identity past kb) := chol(F)^-1 in its lower
+// triangle.  256 threads; F must be complete and visible (after a barrier).
+__device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base, int32_t *__restrict__ info) {
+    const int wave = threadIdx.x >> 6;
+    constexpr int SB = 32, NSB = NB / SB;
+    for (int b = 0; b < NSB; ++b) {
+        const int s = SB * b;
+        if (wave == 0) potrf32(F, s, kb, info_base, info);
+        __syncthreads();
+        // panel blocks i = b+1.. (transposed into block (b, i)) and inverse rows j < b
+        {
+            const int ntask = (NSB - 1 - b) + b;
+            for (int t = wave; t < ntask; t += 4) {
+                f32x16 acc = f32x16{};
+                if (t < NSB - 1 - b) {
+                    const int i = b + 1 + t;
+                    // P_i(m, n) = sum_k A_ib(m, k) X_bb(n, k)
+                    blk_mfma(acc, F, (SB * i) * FLD + s, FLD, 1, s * FLD + s, 1, FLD);
+                    blk_store(acc, F, s, SB * i, 1.f, true);
+                } else {
+                    const int j = t - (NSB - 1 - b);
+                    // M_bj(m, n) = -sum_k X_bb(m, k) S_bj(k, n), in place
+                    blk_mfma(acc, F, s * FLD + s, FLD, 1, s * FLD + SB * j, FLD, 1);
+                    blk_store(acc, F, s, SB * j, -1.f, false);
+                }
+            }
         }
         __syncthreads();
-        float d8[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) d8[q] = dgbuf[q];
-        potrf_tile_column(T, d8, ty, tx, jt, tid, kb, info_base, info, vbuf, std::make_integer_sequence<int, 8>{});
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = 8 * ty + r, cc = 8 * tx + c;
-            dinv[i * NB + cc] = (i < kb && cc < kb && cc <= i) ? T[r][c] : 0.f;
+        // trailing Cholesky blocks (i, c), b < c <= i, then inverse sums (i, j), j <= b
+        {
+            const int nr = NSB - 1 - b;
+            const int nchol = nr * (nr + 1) / 2;
+            const int ntask = nchol + nr * (b + 1);
+            for (int t = wave; t < ntask; t += 4) {
+                f32x16 acc;
+                if (t < nchol) {
+                    int ii = 0;
+                    while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+                    const int i = b + 1 + ii, cc = b + 1 + (t - ii * (ii + 1) / 2);
+                    blk_load(acc, F, SB * i, SB * cc);
+                    // A_ic -= P_i P_c^T with P_x(m, k) at F[(s + k) * FLD + 32x + m]
+                    f32x16 prod = f32x16{};
+                    blk_mfma(prod, F, s * FLD + SB * i, 1, FLD, s * FLD + SB * cc, FLD, 1);
+                    acc -= prod;
+                    blk_store(acc, F, SB * i, SB * cc, 1.f, false);
+                } else {
+                    const int u = t - nchol;
+                    const int i = b + 1 + u / (b + 1), j = u % (b + 1);
+                    if (j < b) {
+                        blk_load(acc, F, SB * i, SB * j);
+                        // S_ij += P_i M_bj
+                        blk_mfma(acc, F, s * FLD + SB * i, 1, FLD, s * FLD + SB * j, FLD, 1);
+                    } else {
+                        acc = f32x16{};
+                        // S_ib = P_i X_bb
+                        blk_mfma(acc, F, s * FLD + SB * i, 1, FLD, s * FLD + s, FLD, 1);
+                    }
+                    blk_store(acc, F, SB * i, SB * j, 1.f, false);
+                }
+            }
         }
+        __syncthreads();
+    }
 }
 
 __global__ __launch_bounds__(256) void potrf_kernel(const float *__restrict__ R, int64_t d, int k0, int kb,
                                                     float *__restrict__ dinv, int32_t *__restrict__ info) {
-    __shared__ __attribute__((aligned(16))) float vbuf[2 * NB];
-    __shared__ float dgbuf[8];
-    potrf_block(R + (int64_t)k0 * d + k0, d, kb, k0, dinv, info, vbuf, dgbuf);
+    __shared__ __attribute__((aligned(16))) float F[NB * FLD];
+    potrf_block_load(R + (int64_t)k0 * d + k0, d, kb, F);
+    __syncthreads();
+    potrf_block_lds(F, kb, k0, info);
+    potrf_block_store(F, kb, dinv);
 }
 
 // part A (row blocks below k): P_i = A_ik Dinv^T -> panel
@@ -207,8 +294,6 @@ __global__ __launch_bounds__(256) void update_kernel(float *__restrict__ R, int6
                                                      const float *__restrict__ dinv_k,
                                                      float *__restrict__ dinv_next, int32_t *__restrict__ info) {
     __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
-    __shared__ __attribute__((aligned(16))) float vbuf[2 * NB];
-    __shared__ float dgbuf[8];
     // work group 0 -> tile (k+1, k+1); 1..k+1 -> (k+1, 0..k); the rest in order
     const int base = (k + 1) * (k + 2) / 2;
     int i, j;
@@ -241,12 +326,30 @@ __global__ __launch_bounds__(256) void update_kernel(float *__restrict__ R, int6
         const float *B = panel + (int64_t)(col0 - k1) * NB;    // B(k, n) = P[col0+n][k]
         gemm_tile<true, true>(acc, A, NB, B, NB, rows, cols, kb, -1.f, true, lds);
     }
-    store_c(acc, C, d, rows, cols);
-    if (blockIdx.x == 0) {
-        // look-ahead: the tile just updated is the next diagonal block
-        __syncthreads();
-        potrf_block(C, d, rows, row0, dinv_next, info, vbuf, dgbuf);
+    if (blockIdx.x != 0) {
+        store_c(acc, C, d, rows, cols);
+        return;
     }
+    // Look-ahead: the tile just updated is the next diagonal block.  Nothing
+    // else reads it from R (the panel step overwrites it with its inverse),
+    // so it goes from the accumulators straight into LDS, identity past kb.
+    // gemm_tile ended on a barrier: the staging area is free.
+    float *F = lds;
+#pragma unroll
+    for (int ma = 0; ma < 2; ++ma)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    int r, c;
+                    tile_rc(ma, mb, a, b, r, c);
+                    F[r * FLD + c] = (r < rows && c < cols) ? acc[ma * 2 + mb][4 * a + b] : (r == c ? 1.f : 0.f);
+                }
+    __syncthreads();
+    potrf_block_lds(F, rows, row0, info);
+    potrf_block_store(F, rows, dinv_next);
 }
 
 __global__ void flip_kernel(float *__restrict__ R, int64_t d, float *__restrict__ ud) {

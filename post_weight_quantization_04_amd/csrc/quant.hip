@@ -14,12 +14,13 @@
 //
 // Layout: a work group owns 16 rows; each row is spread over one 16-lane DPP
 // row (lane c holds column c of the current 16-column chunk), so a wave
-// holds four rows.  The block's W tile and the upper part of the block's U
-// are staged in LDS.  Per column step the current value is broadcast across
-// the 16 lanes with DPP row_newbcast; every lane then computes the same
-// quantization and updates its own column.  After a chunk, its 16 errors
-// (held by every lane of the row) are applied to the rest of the block in
-// LDS with 4-column vector reads of W and U.
+// holds four rows.  The block's W tile, the strict upper part of the block's
+// U and 1/U_kk are staged in LDS.  Per column step the current value is
+// broadcast across the 16 lanes with DPP row_newbcast; every lane then
+// computes the same quantization and updates its own column with a
+// coefficient preloaded into registers for the chunk.  After a chunk, its 16
+// errors (held by every lane of the row) are applied to the rest of the block
+// in LDS with 4-column vector reads of W and U.
 #include "common.h"
 
 #include <algorithm>
@@ -73,34 +74,32 @@ __device__ __forceinline__ void minmax16(float &mn, float &mx) {
 }
 
 struct StepCtx {
-    const float *Ul;
-    int Bp, c0, c, nb;
-    float *Erow;      // E values of the chunk (same in all 16 lanes of a row)
+    int c0, c, nb;
 };
 
+// Column S of the chunk: every lane of the row quantizes the broadcast value
+// and applies the error to its own column (u[S] = U_{i,c} for c > S, else 0).
 template <int S>
 __device__ __forceinline__ void qstep(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
-                                      const Quantizer &Q, const float *__restrict__ uinv_b) {
+                                      const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH]) {
     const int i = cx.c0 + S;
     if (i >= cx.nb) return;                         // uniform: ragged last chunk
     const float x = bcast16<S>(w);
     const float t = x * Q.inv_s;
     const float q = fminf(fmaxf(rintf(t) + Q.z, 0.f), Q.maxq);
     const float wq = Q.s * (q - Q.z);
-    const float err = (x - wq) * uinv_b[i];
+    const float err = (x - wq) * ui[S];
     Ereg[S] = err;
-    if (cx.c == S) {
-        myq = q;
-        myE = err;
-    }
-    if (cx.c > S) w = fmaf(-err, cx.Ul[uidx(i, cx.c0 + cx.c, cx.Bp)], w);
+    myq = (cx.c == S) ? q : myq;
+    myE = (cx.c == S) ? err : myE;
+    w = fmaf(-err, u[S], w);
 }
 
 template <int... S>
 __device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
-                                          const Quantizer &Q, const float *__restrict__ uinv_b,
+                                          const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH],
                                           std::integer_sequence<int, S...>) {
-    (qstep<S>(w, myq, myE, Ereg, cx, Q, uinv_b), ...);
+    (qstep<S>(w, myq, myE, Ereg, cx, Q, u, ui), ...);
 }
 
 // One launch per block [b, e).  Grid: ceil(d_out / 16) groups of 256 threads.
@@ -111,6 +110,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
     const int LW = Bp + 4;                 // W tile row stride (floats)
     float *Wl = lds;                       // [16][LW]
     float *Ul = lds + QROWS * LW;          // packed upper U block
+    float *uil = Ul + usize(Bp);           // 1/U_kk of the block
     const int tid = threadIdx.x;
     const int rl = tid >> 4, c = tid & 15;
     const int64_t row0 = (int64_t)blockIdx.x * QROWS;
@@ -118,25 +118,69 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
     const bool row_ok = row < a.d_out;
     const int64_t d_in = a.d_in, d_out = a.d_out;
 
-    // stage W tile
-    for (int idx = tid; idx < QROWS * Bp; idx += 256) {
-        const int r = idx / Bp, j = idx % Bp;
-        const int64_t gr = row0 + r;
-        Wl[r * LW + j] = (gr < d_out && j < nb) ? a.Wp[gr * d_in + b + j] : 0.f;
-    }
-    // stage U block (upper part, packed)
+    // Stage the W tile, the packed upper part of the U block and 1/U_kk with
+    // 16-byte loads (4-column groups), all of a thread's loads issued before
+    // any is stored: U comes from HBM and one latency per block is the goal.
+    // vec: the block's columns start 16-byte aligned in every row.
+    const bool vec = (d_in % 4 == 0) && (b % 4 == 0);
+    auto load4 = [&](const float *p, int nvalid) -> f32x4 {
+        if (vec && nvalid >= 4) return *(const f32x4 *)p;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (nvalid > 0) v.x = p[0];
+        if (nvalid > 1) v.y = p[1];
+        if (nvalid > 2) v.z = p[2];
+        if (nvalid > 3) v.w = p[3];
+        return v;
+    };
     {
-        const int wv = tid >> 6, ln = tid & 63;
-        for (int i = wv; i < nb; i += 4) {
-            const int j0 = 4 * (i >> 2);
-            const int base = uoff(i, Bp) - j0;
-            for (int j = j0 + ln; j < Bp; j += 64) {
-                float v = 0.f;
-                if (j > i && j < nb) v = a.U[(int64_t)(b + i) * d_in + b + j];
-                else if (j == i) v = a.ud[b + i];
-                Ul[base + j] = v;
+        // W tile: 16 rows x Bp/4 groups, two groups per thread at Bp <= 128
+        const int ngrp = QROWS * (Bp / 4);
+        for (int f0 = 0; f0 < ngrp; f0 += 2 * 256) {
+            f32x4 v[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int f = f0 + tid + 256 * q;
+                const int r = f / (Bp / 4), j = 4 * (f % (Bp / 4));
+                const int64_t gr = row0 + r;
+                v[q] = (f < ngrp && gr < d_out) ? load4(a.Wp + gr * d_in + b + j, nb - j) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int f = f0 + tid + 256 * q;
+                if (f < ngrp) *(f32x4 *)(Wl + (f / (Bp / 4)) * LW + 4 * (f % (Bp / 4))) = v[q];
             }
         }
+    }
+    {
+        // U block: group (i, 4t) for t >= floor(i/4) lands on one aligned packed f32x4
+        const int ngrp = Bp * (Bp / 4);
+        for (int f0 = 0; f0 < ngrp; f0 += 16 * 256) {
+            f32x4 v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int f = f0 + tid + 256 * q;
+                const int i = f / (Bp / 4), j = 4 * (f % (Bp / 4));
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                if (f < ngrp && i < nb && j + 3 > i && j >= 4 * (i >> 2))
+                    x = load4(a.U + (int64_t)(b + i) * d_in + b + j, nb - j);
+                v[q] = x;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int f = f0 + tid + 256 * q;
+                const int i = f / (Bp / 4), j = 4 * (f % (Bp / 4));
+                if (f < ngrp && j >= 4 * (i >> 2)) {
+                    f32x4 x = v[q];
+                    // only the strict upper part is ever read (1/U_kk comes from uil)
+                    x.x = (j + 0 > i) ? x.x : 0.f;
+                    x.y = (j + 1 > i) ? x.y : 0.f;
+                    x.z = (j + 2 > i) ? x.z : 0.f;
+                    x.w = (j + 3 > i) ? x.w : 0.f;
+                    *(f32x4 *)(Ul + uidx(i, j, Bp)) = x;
+                }
+            }
+        }
+        for (int i = tid; i < Bp; i += 256) uil[i] = (i < nb) ? a.uinv[b + i] : 0.f;
     }
     __syncthreads();
 
@@ -151,7 +195,6 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         Q.inv_s = 1.f / s;
         Q.z = row_ok ? a.zeros[gi * d_out + row] : 0.f;
     }
-    const float *uinv_b = a.uinv + b;
 
     for (int c0 = 0; c0 < nb; c0 += CH) {
         const int k = b + c0;
@@ -186,8 +229,23 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         float w = Wl[rl * LW + c0 + c];
         float myq = 0.f, myE = 0.f;
         float Ereg[CH];
-        StepCtx cx{Ul, Bp, c0, c, nb, nullptr};
-        run_chunk(w, myq, myE, Ereg, cx, Q, uinv_b, std::make_integer_sequence<int, CH>{});
+        // this chunk's coefficients in registers, off the dependency chain:
+        // u[S] = U_{c0+S, c0+c} for c > S (0 otherwise), ui[S] = 1/U_{c0+S, c0+S}
+        float u[CH], ui[CH];
+        // the lane's column, opaque to the optimizer: keeps the per-step lane
+        // masks from being hoisted out of the chunk loop (scalar spills)
+        int cl;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(cl) : "v"(c));
+#pragma unroll
+        for (int S = 0; S < CH; ++S) {
+            const int i = c0 + S;
+            const int j = max(c0 + cl, 4 * (i >> 2));       // stays inside row i's packed range
+            const float x = Ul[uidx(min(i, Bp - 1), j, Bp)];
+            u[S] = (cl > S) ? x : 0.f;
+            ui[S] = uil[min(i, Bp - 1)];
+        }
+        StepCtx cx{c0, cl, nb};
+        run_chunk(w, myq, myE, Ereg, cx, Q, u, ui, std::make_integer_sequence<int, CH>{});
         if (row_ok && c0 + c < nb) {
             a.codes[(int64_t)(k + c) * d_out + row] = (uint8_t)myq;
             a.E[(int64_t)(c0 + c) * d_out + row] = myE;
@@ -217,7 +275,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
 
 size_t quant_lds_bytes(int block) {
     const int Bp = roundup16(block);
-    return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp));
+    return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp) + (size_t)Bp);
 }
 
 hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st) {
