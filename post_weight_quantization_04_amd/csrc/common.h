@@ -76,7 +76,7 @@ struct QuantArgs {
     const float *U;        // [d_in][d_in] upper factor (row-major, upper part valid)
     const float *ud;       // [d_in] U diagonal
     const float *uinv;     // [d_in] 1 / U diagonal
-    float *E;              // [B][d_out] block errors
+    float *E;              // [K][d_out] block errors (quant_block writes rows 0..B-1 of the slot it is given)
     uint8_t *codes;        // [d_in][d_out]
     float *scales;         // [G][d_out]
     float *zeros;          // [G][d_out]
@@ -85,7 +85,12 @@ struct QuantArgs {
 };
 size_t quant_lds_bytes(int block);
 hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st);
-hipError_t trail_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st);
+// Blocks whose errors are applied to the far columns together (two-level
+// lazy update): after every block only the next block's columns are updated.
+constexpr int FAR_BLOCKS = 1;
+// W[:, c_begin:c_end) -= E[0:K) (as [K][d_out]) U[u_row0 : u_row0+K, c_begin:c_end)
+hipError_t trail_launch(const QuantArgs &a, int64_t u_row0, int64_t K, int64_t c_begin, int64_t c_end,
+                        hipStream_t st);
 hipError_t pack_launch(const uint8_t *codes, int64_t d_out, int64_t d_in, int bits,
                        uint32_t *Qpacked, hipStream_t st);
 

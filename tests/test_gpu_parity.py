@@ -165,6 +165,8 @@ LAYER_CASES = [
     ("q_proj", 308, 40, 700, 3000, 4, 64, 512, False),         # block wider than the staged block
     ("q_proj", 309, 1, 16, 64, 4, 16, 16, True),               # tiny
     ("up_proj", 310, 33, 250, 1500, 3, 16, 80, True),          # odd block, group 16
+    ("q_proj", 311, 40, 1536, 3000, 4, 512, 512, False),       # groups of 512 over two 256-column internal blocks
+    ("down_proj", 312, 24, 2304, 3000, 4, 768, 768, True),     # groups of 768 over three internal blocks
 ]
 
 
