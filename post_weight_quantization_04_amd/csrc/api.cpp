@@ -149,7 +149,7 @@ Workspace layout(const LayerShape &L, char *base) {
     const int64_t d = L.d_in;
     w.R = (float *)take(sizeof(float) * (size_t)d * d);
     w.Wp = (float *)take(sizeof(float) * (size_t)L.d_out * d);
-    w.E = (float *)take(sizeof(float) * (size_t)L.block_int * L.d_out);
+    w.E = (float *)take(sizeof(float) * (size_t)gptq::FAR_BLOCKS * L.block_int * L.d_out);
     w.codes = (uint8_t *)take((size_t)d * L.d_out);
     w.panel = (float *)take(sizeof(float) * (size_t)d * gptq::FACT_NB);
     w.dinv = (float *)take(sizeof(float) * 2 * gptq::FACT_NB * gptq::FACT_NB);  // ping-pong pair
@@ -345,15 +345,34 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
     qa.bits = bits;
     qa.group = L.group;
     qa.block = L.block_int;
-    for (int64_t b = 0; b < d_in; b += L.block_int) {
-        const int64_t e = std::min<int64_t>(b + L.block_int, d_in);
+    // Errors of the blocks since the last far update are stacked in E (block
+    // t of the batch at rows t*B..); after each block the next block's
+    // columns take all of them, and every FAR_BLOCKS blocks the columns
+    // beyond take them at once.  A group wider than a block takes its
+    // parameters from all its columns at its start, so the pending errors
+    // are also flushed to every column before such a group begins.
+    const int64_t B = L.block_int;
+    int64_t pend0 = 0;   // first column of the oldest pending block
+    int slot = 0;
+    for (int64_t b = 0; b < d_in; b += B) {
+        const int64_t e = std::min<int64_t>(b + B, d_in);
         {
             StageTimer t(5, st);
-            HIPCHECK(gptq::quant_block_launch(qa, b, e, st));
+            gptq::QuantArgs qb = qa;
+            qb.E = w.E + (size_t)slot * B * d_out;
+            HIPCHECK(gptq::quant_block_launch(qb, b, e, st));
         }
-        if (e < d_in) {
-            StageTimer t(6, st);
-            HIPCHECK(gptq::trail_launch(qa, b, e, st));
+        if (e >= d_in) break;
+        const int64_t K = e - pend0;
+        StageTimer t(6, st);
+        const bool wide_group_next = L.group > B && e % L.group == 0;
+        if (slot + 1 == gptq::FAR_BLOCKS || wide_group_next) {
+            HIPCHECK(gptq::trail_launch(qa, pend0, K, e, d_in, st));
+            pend0 = e;
+            slot = 0;
+        } else {
+            HIPCHECK(gptq::trail_launch(qa, pend0, K, e, std::min<int64_t>(e + B, d_in), st));
+            ++slot;
         }
     }
     {
