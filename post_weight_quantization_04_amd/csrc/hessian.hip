@@ -487,7 +487,10 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(const float *__restrict__
 }
 
 // Sum the split partials of each lower tile (fixed order), H += 2*sum, mirror.
-// One work group per 64x64 sub-block.
+// One work group per 64x64 sub-block; VEC (d % 4 == 0): each thread owns four
+// adjacent columns of four rows, read and written 16 bytes at a time, and the
+// mirrored (upper) copy is written as 16-byte runs of four source rows.
+template <bool VEC>
 __global__ __launch_bounds__(256) void hess_reduce_kernel(const float *__restrict__ part, float *__restrict__ H,
                                                           int d, int T, int ntiles, int nsplit) {
     __shared__ float tileT[64][65];
@@ -501,6 +504,63 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const float *__restric
     if (diag && sr < sc) return;
     const int row0 = I * T + sr * 64, col0 = J * T + sc * 64;
     if (row0 >= d || col0 >= d) return;
+    const int64_t tile_stride = (int64_t)ntiles * T * T;
+    const float *pt = part + (int64_t)t * T * T;
+    if (VEC) {
+        const int cg = threadIdx.x & 15, ty = threadIdx.x >> 4;
+        const int c4 = 4 * cg;
+        const int gc = col0 + c4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = ty + 16 * i;
+            const int gr = row0 + rr;
+            const int64_t po = (int64_t)(sr * 64 + rr) * T + sc * 64 + c4;
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int sp = 0; sp < nsplit; ++sp) {
+                const f32x4 p = *(const f32x4 *)(pt + sp * tile_stride + po);
+                s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+            }
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (gr < d && gc < d) {     // d % 4 == 0: the four columns are all in range
+                float *hp = H + (int64_t)gr * d + gc;
+                const f32x4 h = *(const f32x4 *)hp;
+                v = f32x4{h.x + 2.f * s.x, h.y + 2.f * s.y, h.z + 2.f * s.z, h.w + 2.f * s.w};
+                if (!diag || gc + 3 <= gr) {
+                    *(f32x4 *)hp = v;
+                } else {
+                    // diagonal sub-block: the lower part only (the mirror writes the rest)
+                    if (gc + 0 <= gr) hp[0] = v.x; else v.x = 0.f;
+                    if (gc + 1 <= gr) hp[1] = v.y; else v.y = 0.f;
+                    if (gc + 2 <= gr) hp[2] = v.z; else v.z = 0.f;
+                    if (gc + 3 <= gr) hp[3] = v.w; else v.w = 0.f;
+                }
+            }
+            tileT[rr][c4 + 0] = v.x;
+            tileT[rr][c4 + 1] = v.y;
+            tileT[rr][c4 + 2] = v.z;
+            tileT[rr][c4 + 3] = v.w;
+        }
+        __syncthreads();
+        // mirror: H[col0 + cc][row0 + rr .. rr+3] = tileT[rr .. rr+3][cc]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = ty + 16 * i, rr = c4;
+            const int gr = col0 + cc, gcol = row0 + rr;   // destination row, first column
+            if (gr >= d || gcol >= d) continue;
+            float *hp = H + (int64_t)gr * d + gcol;
+            const f32x4 v = {tileT[rr + 0][cc], tileT[rr + 1][cc], tileT[rr + 2][cc], tileT[rr + 3][cc]};
+            if (gcol > gr) {
+                *(f32x4 *)hp = v;
+            } else {
+                if (gcol + 0 > gr) hp[0] = v.x;
+                if (gcol + 1 > gr) hp[1] = v.y;
+                if (gcol + 2 > gr) hp[2] = v.z;
+                if (gcol + 3 > gr) hp[3] = v.w;
+            }
+        }
+        return;
+    }
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int rr = ty; rr < 64; rr += 4) {
         const int r = sr * 64 + rr, c = sc * 64 + tx;
@@ -508,7 +568,7 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const float *__restric
         float v = 0.f;
         if (gr < d && gc < d && !(diag && gc > gr)) {
             float s = 0.f;
-            for (int sp = 0; sp < nsplit; ++sp) s += part[((int64_t)sp * ntiles + t) * T * T + (int64_t)r * T + c];
+            for (int sp = 0; sp < nsplit; ++sp) s += pt[sp * tile_stride + (int64_t)r * T + c];
             v = H[(int64_t)gr * d + gc] + 2.0f * s;
             H[(int64_t)gr * d + gc] = v;
         }
@@ -606,7 +666,10 @@ hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t
 
 hipError_t hessian_reduce_launch(int64_t d, float *H, const float *partials, const HessPlan &p, hipStream_t st) {
     const int sub = p.tile / 64;
-    hess_reduce_kernel<<<p.ntiles * sub * sub, 256, 0, st>>>(partials, H, (int)d, p.tile, p.ntiles, p.s_off);
+    if (d % 4 == 0)
+        hess_reduce_kernel<true><<<p.ntiles * sub * sub, 256, 0, st>>>(partials, H, (int)d, p.tile, p.ntiles, p.s_off);
+    else
+        hess_reduce_kernel<false><<<p.ntiles * sub * sub, 256, 0, st>>>(partials, H, (int)d, p.tile, p.ntiles, p.s_off);
     return hipGetLastError();
 }
 
