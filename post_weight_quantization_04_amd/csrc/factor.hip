@@ -288,6 +288,60 @@ __global__ __launch_bounds__(256) void panel_kernel(float *__restrict__ R, int64
     }
 }
 
+// acc -= P P^T for the 128x128 diagonal tile, P (rows x kb) at p with row
+// stride NB (16-byte aligned rows).  F: NB * FLD floats of LDS.  Accumulator
+// layout as tile_rc: wave (wr, wc) owns the 64x64 quadrant, 2x2 32x32 tiles.
+__device__ __forceinline__ void diag_tile_update(f32x16 (&acc)[4], const float *__restrict__ p, int rows, int kb,
+                                                 float *F) {
+    const int tid = threadIdx.x;
+    // stage P: 128 rows x 32 float4 groups, 16 groups per thread, zero past rows/kb
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        f32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int f = tid + 256 * (8 * half + q);
+            const int m = f >> 5, k4 = 4 * (f & 31);
+            v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (m < rows) {
+                if (k4 + 3 < kb) {
+                    v[q] = *(const f32x4 *)(p + (int64_t)m * NB + k4);
+                } else {
+                    if (k4 + 0 < kb) v[q].x = p[(int64_t)m * NB + k4 + 0];
+                    if (k4 + 1 < kb) v[q].y = p[(int64_t)m * NB + k4 + 1];
+                    if (k4 + 2 < kb) v[q].z = p[(int64_t)m * NB + k4 + 2];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int f = tid + 256 * (8 * half + q);
+            const int m = f >> 5, k4 = 4 * (f & 31);
+            float *dst = F + m * FLD + k4;
+            dst[0] = v[q].x;
+            dst[1] = v[q].y;
+            dst[2] = v[q].z;
+            dst[3] = v[q].w;
+        }
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
+    const float *Ar = F + (wr * 64 + li) * FLD;
+    const float *Br = F + (wc * 64 + li) * FLD;
+#pragma unroll 8
+    for (int kk = 0; kk < NB; kk += 2) {
+        const int k = kk + h;
+        const float a0 = -Ar[k], a1 = -Ar[32 * FLD + k];
+        const float b0 = Br[k], b1 = Br[32 * FLD + k];
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[3], 0, 0, 0);
+    }
+    __syncthreads();   // F is reused by the caller
+}
+
 // Update of step k plus look-ahead factorization of block k+1 (work group 0).
 __global__ __launch_bounds__(256) void update_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
                                                      const float *__restrict__ panel,
@@ -313,7 +367,14 @@ __global__ __launch_bounds__(256) void update_kernel(float *__restrict__ R, int6
     float *C = R + (int64_t)row0 * d + col0;
     const float *A = panel + (int64_t)(row0 - k1) * NB;       // A(m, k) = P[row0+m][k]
     f32x16 acc[4];
-    if (j == k) {
+    if (blockIdx.x == 0) {
+        // The next diagonal tile: C - P P^T with P = the panel rows of block
+        // k+1 (rows x kb, k-contiguous).  P is staged once into LDS ([m][k],
+        // row stride FLD) and feeds both operands; all of its loads and the
+        // tile's own go out before any is consumed.
+        load_c(acc, C, d, rows, cols);
+        diag_tile_update(acc, A, rows, kb, lds);
+    } else if (j == k) {
         zero_acc(acc);
         // B(k, n) = Dinv[k][n]: n-contiguous
         gemm_tile<true, false>(acc, A, NB, dinv_k, NB, rows, cols, kb, 1.f, true, lds);
