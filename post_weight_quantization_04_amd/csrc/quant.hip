@@ -49,8 +49,11 @@ __device__ __forceinline__ float bcast16(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + S, 0xF, 0xF, false));
 }
 
+// lo = -z and hi = maxq - z bound the code relative to the zero point:
+// clamp(rint(t) + z, 0, maxq) - z == clamp(rint(t), -z, maxq - z) exactly (z is
+// an integer), which keeps the add and subtract of z off the column chain.
 struct Quantizer {
-    float s, inv_s, z, maxq;
+    float s, inv_s, z, lo, hi;
 };
 
 __device__ __forceinline__ Quantizer make_quantizer(float xmin, float xmax, float maxq) {
@@ -61,7 +64,18 @@ __device__ __forceinline__ Quantizer make_quantizer(float xmin, float xmax, floa
     Q.s = (xmax - xmin) / maxq;
     Q.z = rintf(-xmin / Q.s);
     Q.inv_s = 1.f / Q.s;
-    Q.maxq = maxq;
+    Q.lo = -Q.z;
+    Q.hi = maxq - Q.z;
+    return Q;
+}
+
+__device__ __forceinline__ Quantizer reuse_quantizer(float s, float z, float maxq) {
+    Quantizer Q;
+    Q.s = s;
+    Q.inv_s = 1.f / s;
+    Q.z = z;
+    Q.lo = -z;
+    Q.hi = maxq - z;
     return Q;
 }
 
@@ -81,16 +95,15 @@ struct StepCtx {
 // and applies the error to its own column (u[S] = U_{i,c} for c > S, else 0).
 template <int S>
 __device__ __forceinline__ void qstep(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
-                                      const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH]) {
+                                      const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH],
+                                      const float (&su)[CH]) {
     const int i = cx.c0 + S;
     if (i >= cx.nb) return;                         // uniform: ragged last chunk
     const float x = bcast16<S>(w);
-    const float t = x * Q.inv_s;
-    const float q = fminf(fmaxf(rintf(t) + Q.z, 0.f), Q.maxq);
-    const float wq = Q.s * (q - Q.z);
-    const float err = (x - wq) * ui[S];
+    const float r = fminf(fmaxf(rintf(x * Q.inv_s), Q.lo), Q.hi);   // code - z
+    const float err = fmaf(-su[S], r, x * ui[S]);                   // (w - s (q - z)) / U_kk
     Ereg[S] = err;
-    myq = (cx.c == S) ? q : myq;
+    myq = (cx.c == S) ? r + Q.z : myq;
     myE = (cx.c == S) ? err : myE;
     w = fmaf(-err, u[S], w);
 }
@@ -98,8 +111,8 @@ __device__ __forceinline__ void qstep(float &w, float &myq, float &myE, float (&
 template <int... S>
 __device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
                                           const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH],
-                                          std::integer_sequence<int, S...>) {
-    (qstep<S>(w, myq, myE, Ereg, cx, Q, u, ui), ...);
+                                          const float (&su)[CH], std::integer_sequence<int, S...>) {
+    (qstep<S>(w, myq, myE, Ereg, cx, Q, u, ui, su), ...);
 }
 
 // One launch per block [b, e).  Grid: ceil(d_out / 16) groups of 256 threads.
@@ -186,14 +199,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
 
     const float maxq = (float)((1 << a.bits) - 1);
     const int g = a.group;
-    Quantizer Q{1.f, 1.f, 0.f, maxq};
+    Quantizer Q = reuse_quantizer(1.f, 0.f, maxq);
     if (b % g != 0) {
         // the current group began in an earlier block: reuse its parameters
         const int64_t gi = b / g;
-        const float s = row_ok ? a.scales[gi * d_out + row] : 1.f;
-        Q.s = s;
-        Q.inv_s = 1.f / s;
-        Q.z = row_ok ? a.zeros[gi * d_out + row] : 0.f;
+        Q = reuse_quantizer(row_ok ? a.scales[gi * d_out + row] : 1.f, row_ok ? a.zeros[gi * d_out + row] : 0.f,
+                            maxq);
     }
 
     for (int c0 = 0; c0 < nb; c0 += CH) {
@@ -244,8 +255,11 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
             u[S] = (cl > S) ? x : 0.f;
             ui[S] = uil[min(i, Bp - 1)];
         }
+        float su[CH];   // s / U_kk (the group's parameters are fixed within a chunk)
+#pragma unroll
+        for (int S = 0; S < CH; ++S) su[S] = Q.s * ui[S];
         StepCtx cx{c0, cl, nb};
-        run_chunk(w, myq, myE, Ereg, cx, Q, u, ui, std::make_integer_sequence<int, CH>{});
+        run_chunk(w, myq, myE, Ereg, cx, Q, u, ui, su, std::make_integer_sequence<int, CH>{});
         if (row_ok && c0 + c < nb) {
             a.codes[(int64_t)(k + c) * d_out + row] = (uint8_t)myq;
             a.E[(int64_t)(c0 + c) * d_out + row] = myE;
