@@ -241,7 +241,11 @@ def test_full_layer_sampled_rows(name, rows):
     torch.cuda.synchronize()
     del Hg
     say("  oracle Hessian")
-    H = O.hessian(np.array_split(X, 32), wl.dtype, wl.d_in)
+    H = None
+    for ci, chunk in enumerate(np.array_split(X, 32)):
+        Hc = O.hessian([chunk], wl.dtype, wl.d_in)   # chunk sums add up (pinned)
+        H = Hc if H is None else H + Hc
+        say(f"    chunk {ci + 1}/32")
     del X
     sel = np.sort(np.random.default_rng(1).choice(wl.d_out, rows, replace=False))
     W0 = O.widen(W[sel], wl.dtype)
