@@ -54,14 +54,15 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the Hessian product kernel from committed
-    rocprofv3 counter runs, or None when absent or taken on other source."""
+def measured_traffic(wl):
+    """Bytes per launch the Hessian product kernel moves beyond L2, from
+    committed rocprofv3 counter runs on this workload, or None when absent,
+    taken on another workload or on other kernel source."""
     try:
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_sha256") != kernel_source_hash():
+    if c.get("kernel_source_sha256") != kernel_source_hash() or not c.get("workload", "").startswith(wl.name + " "):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -204,7 +205,7 @@ def main():
     ms_h, n_h = prof["hessian_product"]
     avg_h = ms_h / max(n_h, 1)
     achieved = f_h / (avg_h * 1e-3) / 1e12 if n_h else None
-    traffic = measured_traffic()
+    traffic = measured_traffic(wl)
     roofline = {"kernel": "hess_bf16_kernel" if wl.dtype == "bf16" else "hess_f32_kernel",
                 "bound": "mfma", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
@@ -218,7 +219,7 @@ def main():
         log(f"bench: oracle {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 
     line = {
-        "metric": "GPTQ layer-quantize ms + TFLOP/s (Hessian+update), 4096x4096, n=262144 tok",
+        "metric": f"GPTQ layer-quantize ms + TFLOP/s (Hessian+update), {wl.d_out}\u00d7{wl.d_in}, n={wl.n} tok",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16+fp32", "data": "synthetic",
