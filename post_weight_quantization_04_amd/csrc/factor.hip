@@ -63,12 +63,22 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // (both halves hold the same column) keeps column c of the working matrix in
 // registers: the trailing Cholesky matrix (both triangles, so that row j can
 // stand in for column j) and, left of the current column, the finished rows
-// of the inverse.  Step j: pivot p = T_jj, il = 1/sqrt(p); row j values
-// r_i = T_ji (i > j) come from lane i by readlane; every column c != j takes
-// T_ic -= r_i (T_jc / p) for i > j, which is the Cholesky update for c > j
-// and the inverse update for c < j; row j of the inverse is finished as
-// T_jc * il (c < j); column j becomes il on the diagonal and -T_ij / p below.
-__device__ __forceinline__ void potrf32(float *F, int s, int kb, int info_base, int32_t *__restrict__ info) {
+// of the inverse.  Step j: pivot p = T_jj, il = 1/sqrt(p); every column
+// c != j takes T_ic -= r_i (T_jc / p) for i > j with r_i = T_ji, which is the
+// Cholesky update for c > j and the inverse update for c < j; row j of the
+// inverse is finished as T_jc * il (c < j) and the diagonal becomes il.
+// Row j (T_jc over all lanes c, pivot included) reaches every lane through
+// bc (2 x 32 floats of LDS, 16-byte aligned): each lane writes its T_jc and
+// reads the row back as broadcast 16-byte reads.  A wave's LDS operations
+// complete in order, so no barrier is needed.  Row j+1 is updated and
+// published first in step j, so the next row's reads overlap this step's
+// remaining updates.
+// Column j of the inverse below the diagonal is -T_ij / p followed by the
+// later inverse updates, all of which are linear in that column alone (their
+// multipliers come from the column itself), so lane j leaves its column as
+// it is at step j and scales rows below the diagonal by -1/p once at the end.
+__device__ __forceinline__ void potrf32(float *F, int s, int kb, int info_base, int32_t *__restrict__ info,
+                                        float *bc) {
     // the lane's column, opaque to the optimizer: otherwise the 64 per-step
     // lane masks (c == j, c < j) are hoisted out of the caller's loop and
     // spill the scalar registers
@@ -77,32 +87,59 @@ __device__ __forceinline__ void potrf32(float *F, int s, int kb, int info_base, 
     float T[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) T[i] = (i >= c) ? F[(s + i) * FLD + s + c] : F[(s + c) * FLD + s + i];
-    int bad = 0;   // first non-positive (or NaN) pivot of this block, 1-based
+    bc[c] = T[0];
+    float r[32];   // row j, read from bc
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const f32x4 v = *(const f32x4 *)(bc + 4 * q);
+        r[4 * q + 0] = v.x;
+        r[4 * q + 1] = v.y;
+        r[4 * q + 2] = v.z;
+        r[4 * q + 3] = v.w;
+    }
+    int bad = 0;       // first non-positive (or NaN) pivot of this block, 1-based
+    float ilc = 0.f;   // this lane's own 1/l_cc
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-        // one step at a time: hoisting the row broadcasts of later steps only
-        // runs the scalar registers out
         __builtin_amdgcn_sched_barrier(0);
-        const float p = readlane_f(T[j], j);
+        const float p = r[j];
         bad = (bad == 0 && !(p > 0.f) && s + j < kb) ? j + 1 : bad;
         // 1/l_jj from the hardware reciprocal square root (about 1 ulp)
         const float il = __builtin_amdgcn_rsqf(p);
         const float il2 = il * il;
         const float tj = T[j];
         const bool me = (c == j);
-        const float w = me ? il2 : tj * il2;
+        const float w = me ? 0.f : tj * il2;
+        ilc = me ? il : ilc;
+        float rn[32];   // row j+1
+        if (j + 1 < 32) {
+            T[j + 1] = fmaf(-r[j + 1], w, T[j + 1]);
+            float *nrow = bc + 32 * ((j + 1) & 1);
+            nrow[c] = T[j + 1];
 #pragma unroll
-        for (int i = j + 1; i < 32; ++i) {
-            const float r = readlane_f(T[j], i);
-            T[i] = fmaf(-r, w, me ? 0.f : T[i]);
-            if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // at most 8 broadcasts in flight
+            for (int q = (j + 1) >> 2; q < 8; ++q) {
+                const f32x4 v = *(const f32x4 *)(nrow + 4 * q);
+                rn[4 * q + 0] = v.x;
+                rn[4 * q + 1] = v.y;
+                rn[4 * q + 2] = v.z;
+                rn[4 * q + 3] = v.w;
+            }
         }
+        // the next row's reads are in flight during this step's updates
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = j + 2; i < 32; ++i) T[i] = fmaf(-r[i], w, T[i]);
         T[j] = me ? il : ((c < j) ? tj * il : tj);
+        if (j + 1 < 32) {
+#pragma unroll
+            for (int i = j + 1; i < 32; ++i) r[i] = rn[i];
+        }
     }
     if (threadIdx.x == 0 && bad != 0 && info[0] == 0) info[0] = info_base + s + bad;
+    const float sc = -ilc * ilc;
     if (threadIdx.x < 32) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) F[(s + i) * FLD + s + c] = (i >= c) ? T[i] : 0.f;
+        for (int i = 0; i < 32; ++i) F[(s + i) * FLD + s + c] = (i > c) ? T[i] * sc : ((i == c) ? T[i] : 0.f);
     }
 }
 
@@ -185,12 +222,14 @@ __device__ __forceinline__ void potrf_block_store(const float *F, int kb, float 
 
 // F (NB x FLD floats in LDS, identity past kb) := chol(F)^-1 in its lower
 // triangle.  256 threads; F must be complete and visible (after a barrier).
-__device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base, int32_t *__restrict__ info) {
+// bc: 64 floats of LDS, 16-byte aligned (row broadcasts of the 32x32 steps).
+__device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base, int32_t *__restrict__ info,
+                                                float *bc) {
     const int wave = threadIdx.x >> 6;
     constexpr int SB = 32, NSB = NB / SB;
     for (int b = 0; b < NSB; ++b) {
         const int s = SB * b;
-        if (wave == 0) potrf32(F, s, kb, info_base, info);
+        if (wave == 0) potrf32(F, s, kb, info_base, info, bc);
         __syncthreads();
         // panel blocks i = b+1.. (transposed into block (b, i)) and inverse rows j < b
         {
@@ -251,9 +290,10 @@ __device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base,
 __global__ __launch_bounds__(256) void potrf_kernel(const float *__restrict__ R, int64_t d, int k0, int kb,
                                                     float *__restrict__ dinv, int32_t *__restrict__ info) {
     __shared__ __attribute__((aligned(16))) float F[NB * FLD];
+    __shared__ __attribute__((aligned(16))) float bc[64];
     potrf_block_load(R + (int64_t)k0 * d + k0, d, kb, F);
     __syncthreads();
-    potrf_block_lds(F, kb, k0, info);
+    potrf_block_lds(F, kb, k0, info, bc);
     potrf_block_store(F, kb, dinv);
 }
 
@@ -343,11 +383,12 @@ __device__ __forceinline__ void diag_tile_update(f32x16 (&acc)[4], const float *
 }
 
 // Update of step k plus look-ahead factorization of block k+1 (work group 0).
-__global__ __launch_bounds__(256) void update_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
+__global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
                                                      const float *__restrict__ panel,
                                                      const float *__restrict__ dinv_k,
                                                      float *__restrict__ dinv_next, int32_t *__restrict__ info) {
     __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
+    __shared__ __attribute__((aligned(16))) float bc[64];
     // work group 0 -> tile (k+1, k+1); 1..k+1 -> (k+1, 0..k); the rest in order
     const int base = (k + 1) * (k + 2) / 2;
     int i, j;
@@ -409,7 +450,7 @@ __global__ __launch_bounds__(256) void update_kernel(float *__restrict__ R, int6
                     F[r * FLD + c] = (r < rows && c < cols) ? acc[ma * 2 + mb][4 * a + b] : (r == c ? 1.f : 0.f);
                 }
     __syncthreads();
-    potrf_block_lds(F, rows, row0, info);
+    potrf_block_lds(F, rows, row0, info, bc);
     potrf_block_store(F, rows, dinv_next);
 }
 
