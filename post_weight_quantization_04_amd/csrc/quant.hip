@@ -15,12 +15,13 @@
 // Layout: a work group owns 16 rows; each row is spread over one 16-lane DPP
 // row (lane c holds column c of the current 16-column chunk), so a wave
 // holds four rows.  The block's W tile, the strict upper part of the block's
-// U and 1/U_kk are staged in LDS.  Per column step the current value is
-// broadcast across the 16 lanes with DPP row_newbcast; every lane then
-// computes the same quantization and updates its own column with a
-// coefficient preloaded into registers for the chunk.  After a chunk, its 16
-// errors (held by every lane of the row) are applied to the rest of the block
-// in LDS with 4-column vector reads of W and U.
+// U, 1/U_kk and the packed rows' offsets are staged in LDS.  Per column step
+// the current value is broadcast across the 16 lanes with DPP row_newbcast;
+// every lane then computes the same quantization and updates its own column
+// with a coefficient preloaded into registers for the chunk.  After a chunk,
+// its 16 x 16 errors go to LDS and the rest of the block takes
+// W[16 rows, j] -= E[16 x 16] U[16, j] as 16 x 16 column tiles on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32), the four waves taking every fourth tile.
 #include "common.h"
 
 #include <algorithm>
@@ -29,6 +30,8 @@
 namespace gptq {
 
 namespace {
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int QROWS = 16;     // rows per work group
 constexpr int CH = 16;        // columns per chunk (= lanes per row)
@@ -43,6 +46,7 @@ __host__ __device__ inline int uoff(int i, int Bp) {
 }
 __host__ __device__ inline int usize(int Bp) { return uoff(Bp, Bp); }
 __device__ __forceinline__ int uidx(int i, int j, int Bp) { return uoff(i, Bp) + j - 4 * (i >> 2); }
+constexpr int ELD = CH + 1;   // row stride of the chunk's error tile in LDS
 
 template <int S>
 __device__ __forceinline__ float bcast16(float v) {
@@ -124,6 +128,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
     float *Wl = lds;                       // [16][LW]
     float *Ul = lds + QROWS * LW;          // packed upper U block
     float *uil = Ul + usize(Bp);           // 1/U_kk of the block
+    int *rbl = (int *)(uil + Bp);          // rbl[i] + j = packed index of U_ij
+    float *El = (float *)(rbl + Bp);       // the chunk's errors [16 rows][ELD]
     const int tid = threadIdx.x;
     const int rl = tid >> 4, c = tid & 15;
     const int64_t row0 = (int64_t)blockIdx.x * QROWS;
@@ -193,7 +199,10 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
                 }
             }
         }
-        for (int i = tid; i < Bp; i += 256) uil[i] = (i < nb) ? a.uinv[b + i] : 0.f;
+        for (int i = tid; i < Bp; i += 256) {
+            uil[i] = (i < nb) ? a.uinv[b + i] : 0.f;
+            rbl[i] = uidx(i, 0, Bp);
+        }
     }
     __syncthreads();
 
@@ -212,7 +221,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         if (k % g == 0) {
             // group start: parameters from the current values of the group's columns
             float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-            if (c0 == 0) {
+            if (c0 + std::min<int64_t>(g, d_in - k) > nb) {
+                // the group reaches past this block: its columns from W
                 const int gl = (int)std::min<int64_t>(g, d_in - k);
                 if (row_ok)
                     for (int j = c; j < gl; j += CH) {
@@ -247,13 +257,29 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         // masks from being hoisted out of the chunk loop (scalar spills)
         int cl;
         asm volatile("v_mov_b32 %0, %1" : "=v"(cl) : "v"(c));
+        {
+            // c0 is a multiple of 16 and Bp of 16: rows c0..c0+15 all exist in
+            // LDS (past nb they hold zeros); max(cl, S) stays inside row
+            // c0+S's packed range, which starts at column c0 + 4 floor(S/4)
+            int rb[CH];
 #pragma unroll
-        for (int S = 0; S < CH; ++S) {
-            const int i = c0 + S;
-            const int j = max(c0 + cl, 4 * (i >> 2));       // stays inside row i's packed range
-            const float x = Ul[uidx(min(i, Bp - 1), j, Bp)];
-            u[S] = (cl > S) ? x : 0.f;
-            ui[S] = uil[min(i, Bp - 1)];
+            for (int q = 0; q < CH / 4; ++q) {
+                const f32x4 x = *(const f32x4 *)(uil + c0 + 4 * q);
+                ui[4 * q + 0] = x.x;
+                ui[4 * q + 1] = x.y;
+                ui[4 * q + 2] = x.z;
+                ui[4 * q + 3] = x.w;
+                const i32x4 y = *(const i32x4 *)(rbl + c0 + 4 * q);
+                rb[4 * q + 0] = y.x;
+                rb[4 * q + 1] = y.y;
+                rb[4 * q + 2] = y.z;
+                rb[4 * q + 3] = y.w;
+            }
+#pragma unroll
+            for (int S = 0; S < CH; ++S) {
+                const float x = Ul[rb[S] + c0 + max(cl, S)];
+                u[S] = (cl > S) ? x : 0.f;
+            }
         }
         float su[CH];   // s / U_kk (the group's parameters are fixed within a chunk)
 #pragma unroll
@@ -264,22 +290,35 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
             a.codes[(int64_t)(k + c) * d_out + row] = (uint8_t)myq;
             a.E[(int64_t)(c0 + c) * d_out + row] = myE;
         }
-        // apply this chunk's errors to the rest of the block
-        const int jr = c0 + CH;
-        const int nsteps = std::min(CH, nb - c0);
-        for (int j = jr + 4 * c; j < nb; j += 4 * CH) {
-            f32x4 wv = *(const f32x4 *)(Wl + rl * LW + j);
+        // apply this chunk's errors to the rest of the block:
+        // W[16 rows, j] -= E[16 rows][16] U[c0 .. c0+15][j] for j >= c0 + 16
+        El[rl * ELD + c] = myE;
+        __syncthreads();
+        {
+            const int wave = tid >> 6, lane = tid & 63;
+            const int li = lane & 15, lk = lane >> 4;
+            // A[i][k] = -E[i][4t + k] at lane i + 16 k
+            float ea[4];
+            int rbk[4];
 #pragma unroll
-            for (int s = 0; s < CH; ++s) {
-                if (s < nsteps) {
-                    const f32x4 u = *(const f32x4 *)(Ul + uidx(c0 + s, j, Bp));
-                    wv.x = fmaf(-Ereg[s], u.x, wv.x);
-                    wv.y = fmaf(-Ereg[s], u.y, wv.y);
-                    wv.z = fmaf(-Ereg[s], u.z, wv.z);
-                    wv.w = fmaf(-Ereg[s], u.w, wv.w);
-                }
+            for (int t = 0; t < 4; ++t) {
+                ea[t] = -El[li * ELD + 4 * t + lk];
+                rbk[t] = rbl[c0 + 4 * t + lk];
             }
-            *(f32x4 *)(Wl + rl * LW + j) = wv;
+            for (int j0 = c0 + CH * (1 + wave); j0 < nb; j0 += 4 * CH) {
+                // D[i][j] at lane 16 (i / 4) + j, register i % 4
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = Wl[(4 * lk + r) * LW + j0 + li];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    // B[k][j] = U[c0 + 4t + k][j0 + j] at lane j + 16 k
+                    const float ub = Ul[rbk[t] + j0 + li];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub, acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Wl[(4 * lk + r) * LW + j0 + li] = acc[r];
+            }
         }
         __syncthreads();
     }
@@ -289,7 +328,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
 
 size_t quant_lds_bytes(int block) {
     const int Bp = roundup16(block);
-    return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp) + (size_t)Bp);
+    return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp) + 2 * (size_t)Bp + (size_t)QROWS * ELD);
 }
 
 hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st) {
