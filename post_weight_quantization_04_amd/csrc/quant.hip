@@ -83,12 +83,22 @@ __device__ __forceinline__ Quantizer reuse_quantizer(float s, float z, float max
     return Q;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// min and max over the 16 lanes of a DPP row, in every lane: rotations by 8
+// and 4 within the row, then swaps of lane pairs 2 and 1 apart in each quad
 __device__ __forceinline__ void minmax16(float &mn, float &mx) {
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, m, 16));
-    }
+    mn = fminf(mn, dpp_f<0x128>(mn));
+    mx = fmaxf(mx, dpp_f<0x128>(mx));
+    mn = fminf(mn, dpp_f<0x124>(mn));
+    mx = fmaxf(mx, dpp_f<0x124>(mx));
+    mn = fminf(mn, dpp_f<0x4E>(mn));
+    mx = fmaxf(mx, dpp_f<0x4E>(mx));
+    mn = fminf(mn, dpp_f<0xB1>(mn));
+    mx = fmaxf(mx, dpp_f<0xB1>(mx));
 }
 
 struct StepCtx {
@@ -96,27 +106,30 @@ struct StepCtx {
 };
 
 // Column S of the chunk: every lane of the row quantizes the broadcast value
-// and applies the error to its own column (u[S] = U_{i,c} for c > S, else 0).
-template <int S>
-__device__ __forceinline__ void qstep(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
-                                      const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH],
+// x and applies the error to its own column c:
+//   w_c -= E U_{i,c} = w_c - x U_{i,c}/U_ii + r s U_{i,c}/U_ii
+// with uu[S] = U_{i,c}/U_ii and sv[S] = s U_{i,c}/U_ii (both 0 for c <= S),
+// so that only the code (round, clamp) and one fma stay on the chain from
+// one column to the next.  The error itself, (x - s r)/U_ii, is only output.
+template <int S, bool RAGGED>
+__device__ __forceinline__ void qstep(float &w, float &myq, float &myE, const StepCtx &cx, const Quantizer &Q,
+                                      const float (&uu)[CH], const float (&sv)[CH], const float (&ui)[CH],
                                       const float (&su)[CH]) {
-    const int i = cx.c0 + S;
-    if (i >= cx.nb) return;                         // uniform: ragged last chunk
+    if (RAGGED && cx.c0 + S >= cx.nb) return;       // uniform: ragged last chunk
     const float x = bcast16<S>(w);
-    const float r = fminf(fmaxf(rintf(x * Q.inv_s), Q.lo), Q.hi);   // code - z
-    const float err = fmaf(-su[S], r, x * ui[S]);                   // (w - s (q - z)) / U_kk
-    Ereg[S] = err;
+    const float r = __builtin_amdgcn_fmed3f(rintf(x * Q.inv_s), Q.lo, Q.hi);   // code - z
+    const float t = fmaf(-x, uu[S], w);
+    const float err = fmaf(-su[S], r, x * ui[S]);                              // (w - s (q - z)) / U_kk
     myq = (cx.c == S) ? r + Q.z : myq;
     myE = (cx.c == S) ? err : myE;
-    w = fmaf(-err, u[S], w);
+    w = fmaf(r, sv[S], t);
 }
 
-template <int... S>
-__device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, float (&Ereg)[CH], const StepCtx &cx,
-                                          const Quantizer &Q, const float (&u)[CH], const float (&ui)[CH],
+template <bool RAGGED, int... S>
+__device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, const StepCtx &cx, const Quantizer &Q,
+                                          const float (&uu)[CH], const float (&sv)[CH], const float (&ui)[CH],
                                           const float (&su)[CH], std::integer_sequence<int, S...>) {
-    (qstep<S>(w, myq, myE, Ereg, cx, Q, u, ui, su), ...);
+    (qstep<S, RAGGED>(w, myq, myE, cx, Q, uu, sv, ui, su), ...);
 }
 
 // One launch per block [b, e).  Grid: ceil(d_out / 16) groups of 256 threads.
@@ -140,10 +153,13 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
     // Stage the W tile, the packed upper part of the U block and 1/U_kk with
     // 16-byte loads (4-column groups), all of a thread's loads issued before
     // any is stored: U comes from HBM and one latency per block is the goal.
-    // vec: the block's columns start 16-byte aligned in every row.
-    const bool vec = (d_in % 4 == 0) && (b % 4 == 0);
+    // Thread mapping without divisions: lane & 31 picks the 4-column group
+    // (plus 32 per half for blocks wider than 128 columns), tid >> 5 plus 8q
+    // the row.  full: every group of the block is 4 valid, 16-byte aligned
+    // columns, so no load needs a per-column bound.
+    const bool full = (d_in % 4 == 0) && (b % 4 == 0) && (nb % 4 == 0);
     auto load4 = [&](const float *p, int nvalid) -> f32x4 {
-        if (vec && nvalid >= 4) return *(const f32x4 *)p;
+        if (full) return *(const f32x4 *)p;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (nvalid > 0) v.x = p[0];
         if (nvalid > 1) v.y = p[1];
@@ -151,57 +167,71 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         if (nvalid > 3) v.w = p[3];
         return v;
     };
+    const int G = Bp / 4;                  // 4-column groups per row (<= 64)
+    const int jg0 = tid & 31, ri = tid >> 5;
     {
-        // W tile: 16 rows x Bp/4 groups, two groups per thread at Bp <= 128
-        const int ngrp = QROWS * (Bp / 4);
-        for (int f0 = 0; f0 < ngrp; f0 += 2 * 256) {
-            f32x4 v[2];
+        const int nhalf = (G + 31) / 32;   // 1 or 2
+        f32x4 wv[2][2], uv[2][16];
+        // W tile: 16 rows
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int f = f0 + tid + 256 * q;
-                const int r = f / (Bp / 4), j = 4 * (f % (Bp / 4));
+                const int jg = jg0 + 32 * hh, r = ri + 8 * q, j = 4 * jg;
                 const int64_t gr = row0 + r;
-                v[q] = (f < ngrp && gr < d_out) ? load4(a.Wp + gr * d_in + b + j, nb - j) : f32x4{0.f, 0.f, 0.f, 0.f};
+                wv[hh][q] = (hh < nhalf && jg < G && gr < d_out && j < nb) ? load4(a.Wp + gr * d_in + b + j, nb - j)
+                                                                          : f32x4{0.f, 0.f, 0.f, 0.f};
             }
+        // U block rows 0..127 (rows 128..255 of a wider block in a second pass)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int jg = jg0 + 32 * hh, i = ri + 8 * q, j = 4 * jg;
+                uv[hh][q] = (hh < nhalf && jg < G && i < nb && j + 3 > i && j < nb)
+                                ? load4(a.U + (int64_t)(b + i) * d_in + b + j, nb - j)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        const float uiv = (tid < nb) ? a.uinv[b + tid] : 0.f;   // Bp <= 256: one per thread
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int f = f0 + tid + 256 * q;
-                if (f < ngrp) *(f32x4 *)(Wl + (f / (Bp / 4)) * LW + 4 * (f % (Bp / 4))) = v[q];
+                const int jg = jg0 + 32 * hh, r = ri + 8 * q;
+                if (hh < nhalf && jg < G) *(f32x4 *)(Wl + r * LW + 4 * jg) = wv[hh][q];
             }
+        // only the strict upper part of U is ever read (1/U_kk comes from uil);
+        // row i's packed range starts at column 4 floor(i/4)
+        auto store_u = [&](int i, int jg, f32x4 x) {
+            const int j = 4 * jg;
+            if (i < Bp && jg < G && j >= 4 * (i >> 2)) {
+                x.x = (j + 0 > i) ? x.x : 0.f;
+                x.y = (j + 1 > i) ? x.y : 0.f;
+                x.z = (j + 2 > i) ? x.z : 0.f;
+                x.w = (j + 3 > i) ? x.w : 0.f;
+                *(f32x4 *)(Ul + uidx(i, j, Bp)) = x;
+            }
+        };
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (hh < nhalf) store_u(ri + 8 * q, jg0 + 32 * hh, uv[hh][q]);
+        if (tid < Bp) {
+            uil[tid] = uiv;
+            rbl[tid] = uidx(tid, 0, Bp);
         }
-    }
-    {
-        // U block: group (i, 4t) for t >= floor(i/4) lands on one aligned packed f32x4
-        const int ngrp = Bp * (Bp / 4);
-        for (int f0 = 0; f0 < ngrp; f0 += 16 * 256) {
-            f32x4 v[16];
+        if (Bp > 128) {
+            // rows 128..Bp-1 (only their columns >= 128 are in the packed range)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int f = f0 + tid + 256 * q;
-                const int i = f / (Bp / 4), j = 4 * (f % (Bp / 4));
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-                if (f < ngrp && i < nb && j + 3 > i && j >= 4 * (i >> 2))
-                    x = load4(a.U + (int64_t)(b + i) * d_in + b + j, nb - j);
-                v[q] = x;
+                const int jg = jg0 + 32, i = 128 + ri + 8 * q, j = 4 * jg;
+                uv[0][q] = (jg < G && i < nb && j + 3 > i && j < nb)
+                               ? load4(a.U + (int64_t)(b + i) * d_in + b + j, nb - j)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int f = f0 + tid + 256 * q;
-                const int i = f / (Bp / 4), j = 4 * (f % (Bp / 4));
-                if (f < ngrp && j >= 4 * (i >> 2)) {
-                    f32x4 x = v[q];
-                    // only the strict upper part is ever read (1/U_kk comes from uil)
-                    x.x = (j + 0 > i) ? x.x : 0.f;
-                    x.y = (j + 1 > i) ? x.y : 0.f;
-                    x.z = (j + 2 > i) ? x.z : 0.f;
-                    x.w = (j + 3 > i) ? x.w : 0.f;
-                    *(f32x4 *)(Ul + uidx(i, j, Bp)) = x;
-                }
-            }
-        }
-        for (int i = tid; i < Bp; i += 256) {
-            uil[i] = (i < nb) ? a.uinv[b + i] : 0.f;
-            rbl[i] = uidx(i, 0, Bp);
+            for (int q = 0; q < 16; ++q) store_u(128 + ri + 8 * q, jg0 + 32, uv[0][q]);
         }
     }
     __syncthreads();
@@ -249,7 +279,6 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         }
         float w = Wl[rl * LW + c0 + c];
         float myq = 0.f, myE = 0.f;
-        float Ereg[CH];
         // this chunk's coefficients in registers, off the dependency chain:
         // u[S] = U_{c0+S, c0+c} for c > S (0 otherwise), ui[S] = 1/U_{c0+S, c0+S}
         float u[CH], ui[CH];
@@ -281,11 +310,20 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
                 u[S] = (cl > S) ? x : 0.f;
             }
         }
-        float su[CH];   // s / U_kk (the group's parameters are fixed within a chunk)
+        // s / U_kk, U_kc / U_kk and s U_kc / U_kk (the group's parameters are
+        // fixed within a chunk)
+        float su[CH], uu[CH], sv[CH];
 #pragma unroll
-        for (int S = 0; S < CH; ++S) su[S] = Q.s * ui[S];
+        for (int S = 0; S < CH; ++S) {
+            su[S] = Q.s * ui[S];
+            uu[S] = u[S] * ui[S];
+            sv[S] = u[S] * su[S];
+        }
         StepCtx cx{c0, cl, nb};
-        run_chunk(w, myq, myE, Ereg, cx, Q, u, ui, su, std::make_integer_sequence<int, CH>{});
+        if (c0 + CH <= nb)
+            run_chunk<false>(w, myq, myE, cx, Q, uu, sv, ui, su, std::make_integer_sequence<int, CH>{});
+        else
+            run_chunk<true>(w, myq, myE, cx, Q, uu, sv, ui, su, std::make_integer_sequence<int, CH>{});
         if (row_ok && c0 + c < nb) {
             a.codes[(int64_t)(k + c) * d_out + row] = (uint8_t)myq;
             a.E[(int64_t)(c0 + c) * d_out + row] = myE;
@@ -339,6 +377,7 @@ hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStrea
         if (err != hipSuccess) return err;
         attr_done = true;
     }
+    if (e - b < 1 || e - b > 256) return hipErrorInvalidValue;   // the kernel stages at most 256 columns
     const size_t lds = quant_lds_bytes((int)(e - b));
     const unsigned grid = (unsigned)cdiv(a.d_out, QROWS);
     quant_block_kernel<<<grid, 256, lds, st>>>(a, (int)b, (int)e);
