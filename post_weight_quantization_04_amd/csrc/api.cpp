@@ -346,11 +346,12 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
     qa.group = L.group;
     qa.block = L.block_int;
     // Errors of the blocks since the last far update are stacked in E (block
-    // t of the batch at rows t*B..); after each block the next block's
-    // columns take all of them, and every FAR_BLOCKS blocks the columns
-    // beyond take them at once.  A group wider than a block takes its
-    // parameters from all its columns at its start, so the pending errors
-    // are also flushed to every column before such a group begins.
+    // t of the batch at rows t*B..).  Each block's in-block kernel first
+    // applies all of them to its own columns (the near update), and every
+    // FAR_BLOCKS blocks one product applies them to every column beyond.  A
+    // group wider than a block takes its parameters from all its columns at
+    // its start, so the pending errors are also flushed to every column
+    // before such a group begins.
     const int64_t B = L.block_int;
     int64_t pend0 = 0;   // first column of the oldest pending block
     int slot = 0;
@@ -360,18 +361,19 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
             StageTimer t(5, st);
             gptq::QuantArgs qb = qa;
             qb.E = w.E + (size_t)slot * B * d_out;
+            qb.En = w.E;
+            qb.near_row0 = pend0;
+            qb.near_k = (int)(b - pend0);
             HIPCHECK(gptq::quant_block_launch(qb, b, e, st));
         }
         if (e >= d_in) break;
-        const int64_t K = e - pend0;
-        StageTimer t(6, st);
         const bool wide_group_next = L.group > B && e % L.group == 0;
         if (slot + 1 == gptq::FAR_BLOCKS || wide_group_next) {
-            HIPCHECK(gptq::trail_launch(qa, pend0, K, e, d_in, st));
+            StageTimer t(6, st);
+            HIPCHECK(gptq::trail_launch(qa, pend0, e - pend0, e, d_in, st));
             pend0 = e;
             slot = 0;
         } else {
-            HIPCHECK(gptq::trail_launch(qa, pend0, K, e, std::min<int64_t>(e + B, d_in), st));
             ++slot;
         }
     }

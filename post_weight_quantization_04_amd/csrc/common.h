@@ -77,6 +77,9 @@ struct QuantArgs {
     const float *ud;       // [d_in] U diagonal
     const float *uinv;     // [d_in] 1 / U diagonal
     float *E;              // [K][d_out] block errors (quant_block writes rows 0..B-1 of the slot it is given)
+    const float *En;       // [near_k][d_out] errors of the pending blocks (quant_block reads them)
+    int64_t near_row0;     // first column of the pending blocks (their rows of U)
+    int near_k;            // pending columns; quant_block first applies them to its own columns
     uint8_t *codes;        // [d_in][d_out]
     float *scales;         // [G][d_out]
     float *zeros;          // [G][d_out]
@@ -86,8 +89,10 @@ struct QuantArgs {
 size_t quant_lds_bytes(int block);
 hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st);
 // Blocks whose errors are applied to the far columns together (two-level
-// lazy update): after every block only the next block's columns are updated.
-constexpr int FAR_BLOCKS = 1;
+// lazy update): each block's in-block kernel first takes the pending blocks'
+// errors on its own columns, and every FAR_BLOCKS blocks one product applies
+// all pending errors to the columns beyond.
+constexpr int FAR_BLOCKS = 2;
 // W[:, c_begin:c_end) -= E[0:K) (as [K][d_out]) U[u_row0 : u_row0+K, c_begin:c_end)
 hipError_t trail_launch(const QuantArgs &a, int64_t u_row0, int64_t K, int64_t c_begin, int64_t c_end,
                         hipStream_t st);

@@ -236,6 +236,53 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
     }
     __syncthreads();
 
+    if (a.near_k > 0) {
+        // The pending blocks' errors on this block's columns:
+        //   W[16 rows][j] -= sum_{k < near_k} En[k][row] U[near_row0 + k][b + j]
+        // as 16 x 16 tiles on v_mfma_f32_16x16x4_f32 (A[i][k] at lane i + 16k,
+        // B[k][j] at lane j + 16k, D[i][j] at lane 16 (i/4) + j, register
+        // i % 4).  Wave w takes column tiles w and w + 4 (then w + 8, w + 12
+        // for blocks past 128 columns); k goes in batches of 64 whose
+        // operand loads (from L2) are all issued before their products.
+        const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+        const int64_t ra = row0 + li;
+        const bool ra_ok = ra < d_out;
+        const float *ep = a.En + ra;                                   // En[k][ra]
+        const float *up = a.U + a.near_row0 * d_in + b;                 // U[near_row0 + k][b + j]
+        const int nk = a.near_k;
+        for (int jp = 16 * wave; jp < nb; jp += 128) {
+            const int j1 = jp + 64;                                     // second tile of the pair
+            for (int k0 = 0; k0 < nk; k0 += 64) {
+                float ea[16], ub0[16], ub1[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const int k = k0 + 4 * t + lk;
+                    const bool k_ok = k < nk;
+                    ea[t] = (k_ok && ra_ok) ? -ep[(int64_t)k * d_out] : 0.f;
+                    ub0[t] = (k_ok && jp + li < nb) ? up[(int64_t)k * d_in + jp + li] : 0.f;
+                    ub1[t] = (k_ok && j1 + li < nb) ? up[(int64_t)k * d_in + j1 + li] : 0.f;
+                }
+                f32x4 acc0, acc1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc0[r] = Wl[(4 * lk + r) * LW + jp + li];
+                    acc1[r] = (j1 < Bp) ? Wl[(4 * lk + r) * LW + j1 + li] : 0.f;
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub0[t], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub1[t], acc1, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    Wl[(4 * lk + r) * LW + jp + li] = acc0[r];
+                    if (j1 < Bp) Wl[(4 * lk + r) * LW + j1 + li] = acc1[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
     const float maxq = (float)((1 << a.bits) - 1);
     const int g = a.group;
     Quantizer Q = reuse_quantizer(1.f, 0.f, maxq);
