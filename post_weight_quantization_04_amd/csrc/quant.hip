@@ -245,22 +245,31 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
         // for blocks past 128 columns); k goes in batches of 64 whose
         // operand loads (from L2) are all issued before their products.
         const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+        // every load reads an address clamped into range and the value is
+        // zeroed afterwards, so that the loads carry no branches and go out
+        // together
         const int64_t ra = row0 + li;
         const bool ra_ok = ra < d_out;
-        const float *ep = a.En + ra;                                   // En[k][ra]
+        const float *ep = a.En + (ra_ok ? ra : d_out - 1);              // En[k][ra]
         const float *up = a.U + a.near_row0 * d_in + b;                 // U[near_row0 + k][b + j]
         const int nk = a.near_k;
         for (int jp = 16 * wave; jp < nb; jp += 128) {
             const int j1 = jp + 64;                                     // second tile of the pair
+            const bool c0_ok = jp + li < nb, c1_ok = j1 + li < nb;
+            const int cc0 = c0_ok ? jp + li : nb - 1, cc1 = c1_ok ? j1 + li : nb - 1;
             for (int k0 = 0; k0 < nk; k0 += 64) {
                 float ea[16], ub0[16], ub1[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     const int k = k0 + 4 * t + lk;
                     const bool k_ok = k < nk;
-                    ea[t] = (k_ok && ra_ok) ? -ep[(int64_t)k * d_out] : 0.f;
-                    ub0[t] = (k_ok && jp + li < nb) ? up[(int64_t)k * d_in + jp + li] : 0.f;
-                    ub1[t] = (k_ok && j1 + li < nb) ? up[(int64_t)k * d_in + j1 + li] : 0.f;
+                    const int64_t kc = k_ok ? k : nk - 1;
+                    const float e = ep[kc * d_out];
+                    const float u0 = up[kc * d_in + cc0];
+                    const float u1 = up[kc * d_in + cc1];
+                    ea[t] = (k_ok && ra_ok) ? -e : 0.f;
+                    ub0[t] = (k_ok && c0_ok) ? u0 : 0.f;
+                    ub1[t] = (k_ok && c1_ok) ? u1 : 0.f;
                 }
                 f32x4 acc0, acc1;
 #pragma unroll
