@@ -374,10 +374,11 @@ __device__ __forceinline__ void diag_tile_update(f32x16 (&acc)[4], const float *
         const int k = kk + h;
         const float a0 = -Ar[k], a1 = -Ar[32 * FLD + k];
         const float b0 = Br[k], b1 = Br[32 * FLD + k];
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[3], 0, 0, 0);
+        // transposed products, as in the tile product (accumulator layout of tile_rc)
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[3], 0, 0, 0);
     }
     __syncthreads();   // F is reused by the caller
 }

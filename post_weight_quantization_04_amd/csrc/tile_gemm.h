@@ -1,5 +1,5 @@
-// fp32-MFMA 128x128 tile product shared by the factorization and the
-// trailing update: acc += alpha * A(128 x K) * B(K x 128).
+// fp32-MFMA 128x128 tile product of the factorization:
+// acc += alpha * A(128 x K) * B(K x 128).
 //
 // Operands are strided views: A(m, k) = A[m*lda + k] when A is k-contiguous,
 // else A[k*lda + m]; B(k, n) = B[k*ldb + n] when B is n-contiguous, else
@@ -8,8 +8,10 @@
 // chunk's global loads overlap the current chunk's MFMAs.  Interior tiles
 // with aligned rows use 16-byte loads; edges fall back to guarded scalar
 // loads.  Four waves own 64x64 quadrants, each as 2x2 v_mfma_f32_32x32x2_f32
-// tiles; accumulator layout: lane (h, li), register 4a+b <-> row 8a+4h+b,
-// column li of the 32x32 sub-tile.
+// tiles computed transposed (D = B^T A^T), so that the accumulator of lane
+// (h, li), register 4a+b, holds row li, column 8a+4h+b of the 32x32 sub-tile:
+// every lane owns four consecutive columns of a row, and C moves with
+// 16-byte accesses.
 #pragma once
 #include "common.h"
 
@@ -32,8 +34,8 @@ __device__ __forceinline__ void tile_coords(int t, int &I, int &J) {
 __device__ __forceinline__ void tile_rc(int ma, int mb, int a, int b, int &r, int &c) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
-    r = wr * 64 + ma * 32 + 8 * a + 4 * h + b;
-    c = wc * 64 + mb * 32 + li;
+    r = wr * 64 + ma * 32 + li;
+    c = wc * 64 + mb * 32 + 8 * a + 4 * h + b;
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4]) {
@@ -41,34 +43,62 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4]) {
     for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 }
 
+// C tile (rows x cols at C, row stride ldc) <-> accumulators.  Registers
+// 4a .. 4a+3 are four consecutive columns of one row: 16-byte accesses when
+// they are all inside the tile and C's rows are 16-byte aligned.
 __device__ __forceinline__ void load_c(f32x16 (&acc)[4], const float *C, int64_t ldc, int rows, int cols) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && (ldc % 4 == 0);
 #pragma unroll
     for (int ma = 0; ma < 2; ++ma)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    int r, c;
-                    tile_rc(ma, mb, a, b, r, c);
-                    acc[ma * 2 + mb][4 * a + b] = (r < rows && c < cols) ? C[r * ldc + c] : 0.f;
+            for (int a = 0; a < 4; ++a) {
+                int r, c;
+                tile_rc(ma, mb, a, 0, r, c);
+                const float *src = C + (int64_t)r * ldc + c;
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                if (r < rows) {
+                    if (vec && c + 3 < cols) {
+                        x = *(const f32x4 *)src;
+                    } else {
+                        if (c + 0 < cols) x.x = src[0];
+                        if (c + 1 < cols) x.y = src[1];
+                        if (c + 2 < cols) x.z = src[2];
+                        if (c + 3 < cols) x.w = src[3];
+                    }
                 }
+                acc[ma * 2 + mb][4 * a + 0] = x.x;
+                acc[ma * 2 + mb][4 * a + 1] = x.y;
+                acc[ma * 2 + mb][4 * a + 2] = x.z;
+                acc[ma * 2 + mb][4 * a + 3] = x.w;
+            }
 }
 
 __device__ __forceinline__ void store_c(const f32x16 (&acc)[4], float *C, int64_t ldc, int rows, int cols) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && (ldc % 4 == 0);
 #pragma unroll
     for (int ma = 0; ma < 2; ++ma)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    int r, c;
-                    tile_rc(ma, mb, a, b, r, c);
-                    if (r < rows && c < cols) C[r * ldc + c] = acc[ma * 2 + mb][4 * a + b];
+            for (int a = 0; a < 4; ++a) {
+                int r, c;
+                tile_rc(ma, mb, a, 0, r, c);
+                float *dst = C + (int64_t)r * ldc + c;
+                const f32x4 x = {acc[ma * 2 + mb][4 * a + 0], acc[ma * 2 + mb][4 * a + 1],
+                                 acc[ma * 2 + mb][4 * a + 2], acc[ma * 2 + mb][4 * a + 3]};
+                if (r < rows) {
+                    if (vec && c + 3 < cols) {
+                        *(f32x4 *)dst = x;
+                    } else {
+                        if (c + 0 < cols) dst[0] = x.x;
+                        if (c + 1 < cols) dst[1] = x.y;
+                        if (c + 2 < cols) dst[2] = x.z;
+                        if (c + 3 < cols) dst[3] = x.w;
+                    }
                 }
+            }
 }
 
 // One operand chunk: 32 (k) x 128 (m or n) values held as 16 floats per thread.
@@ -180,7 +210,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4], const float *A, int6
             for (int ma = 0; ma < 2; ++ma)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
-                    acc[ma * 2 + mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[ma], fb[mb], acc[ma * 2 + mb], 0, 0, 0);
+                    acc[ma * 2 + mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[mb], fa[ma], acc[ma * 2 + mb], 0, 0, 0);
         }
         if (more) {
             ca.store(lds + (2 * (buf ^ 1)) * GSTAGE, alpha);
