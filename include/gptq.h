@@ -141,8 +141,9 @@ GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float dam
                                 void *stream);
 
 /* ---------------------------------------------------------------------------
- * Stage timing (tracing aid).  When enabled, every call records a pair of
- * hipEvents around each stage's launches on the caller's stream; reading
+ * Stage timing (tracing aid).  gptq_profile_enable(stage_mask): bit s set
+ * makes every later call record a pair of hipEvents around stage s's launches
+ * on the caller's stream (GPTQ_PROFILE_ALL: every stage; 0: none).  Reading
  * waits for those events and returns the summed GPU time per stage since the
  * last reset.  Process-wide state: enable it only while one thread drives
  * the library.  Stages:
@@ -152,12 +153,13 @@ GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float dam
  *   6 trailing-update kernels      7 bit packing
  * ------------------------------------------------------------------------- */
 #define GPTQ_NUM_STAGES 8
+#define GPTQ_PROFILE_ALL ((1 << GPTQ_NUM_STAGES) - 1)
 typedef struct {
     double ms[GPTQ_NUM_STAGES];        /* summed GPU milliseconds */
     int64_t launches[GPTQ_NUM_STAGES]; /* timed launch groups */
 } gptq_profile;
 
-GPTQ_API void gptq_profile_enable(int on);
+GPTQ_API void gptq_profile_enable(int stage_mask);
 GPTQ_API gptq_status gptq_profile_read(gptq_profile *out, int reset);
 GPTQ_API const char *gptq_profile_stage_name(int stage);
 

@@ -86,9 +86,14 @@ class _Profile(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * NUM_STAGES), ("launches", ctypes.c_int64 * NUM_STAGES)]
 
 
-def profile_enable(on: bool = True) -> None:
-    """Record hipEvents around every stage launch (see gptq_profile_enable)."""
-    _lib().gptq_profile_enable(int(bool(on)))
+def profile_enable(on=True) -> None:
+    """Record hipEvents around stage launches (see gptq_profile_enable): True
+    times every stage, False none, an int is the stage bit mask."""
+    if isinstance(on, bool):
+        mask = (1 << NUM_STAGES) - 1 if on else 0
+    else:
+        mask = int(on)
+    _lib().gptq_profile_enable(mask)
 
 
 def profile_read(reset: bool = True) -> dict:

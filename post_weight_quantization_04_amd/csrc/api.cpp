@@ -41,7 +41,7 @@ gptq_status fail(gptq_status s, const char *fmt, ...) {
 // stage timing
 // ---------------------------------------------------------------------------
 struct Profiler {
-    bool on = false;
+    unsigned mask = 0;   // bit s: stage s is timed
     std::mutex mu;
     std::vector<hipEvent_t> pool;
     struct Pending { int stage; hipEvent_t a, b; };
@@ -68,7 +68,7 @@ struct StageTimer {
     hipStream_t st;
     hipEvent_t a = nullptr;
     StageTimer(int s, hipStream_t stream) : stage(s), st(stream) {
-        if (!g_prof.on) return;
+        if (!((g_prof.mask >> s) & 1u)) return;
         std::lock_guard<std::mutex> lk(g_prof.mu);
         a = g_prof.get();
         if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
@@ -200,9 +200,9 @@ extern "C" {
 
 const char *gptq_version(void) { return "libgptq 0.1 (gfx950)"; }
 
-void gptq_profile_enable(int on) {
+void gptq_profile_enable(int stage_mask) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    g_prof.on = on != 0;
+    g_prof.mask = (unsigned)stage_mask & ((1u << GPTQ_NUM_STAGES) - 1u);
 }
 
 const char *gptq_profile_stage_name(int stage) {
