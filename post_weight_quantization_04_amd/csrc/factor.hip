@@ -297,29 +297,158 @@ __global__ __launch_bounds__(256) void potrf_kernel(const float *__restrict__ R,
     potrf_block_store(F, kb, dinv);
 }
 
-// part A (row blocks below k): P_i = A_ik Dinv^T -> panel
-// part B (column tiles left of k): M_kj = -Dinv S_kj (in place)
+// Narrow operand chunk for the strip products: 32 (k) x 32 (x) values, four
+// per thread.  KCONTIG: element (x, k) at p[x*ld + k] (thread t: x = t/8,
+// k quad t%8); otherwise at p[k*ld + x] (x quad t%8, k = t/8).  Staged in
+// LDS as [k][x] with row stride 33.
+constexpr int SLD = 33;
+template <bool KCONTIG>
+struct NChunk {
+    float v[4];
+    __device__ __forceinline__ void load(const float *p, int64_t ld, int kbase, int xlim, int klim, bool fast) {
+        const int t = threadIdx.x;
+        if (KCONTIG) {
+            const int x = t >> 3, kq = (t & 7) * 4;
+            const float *src = p + (int64_t)x * ld + kbase + kq;
+            if (fast) {
+                const f32x4 q = *(const f32x4 *)src;
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (x < xlim && kbase + kq + e < klim) ? src[e] : 0.f;
+            }
+        } else {
+            const int xq = (t & 7) * 4, k = t >> 3;
+            const float *src = p + (int64_t)(kbase + k) * ld + xq;
+            if (fast) {
+                const f32x4 q = *(const f32x4 *)src;
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (kbase + k < klim && xq + e < xlim) ? src[e] : 0.f;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float *st, float alpha) const {
+        const int t = threadIdx.x;
+        if (KCONTIG) {
+            const int x = t >> 3, kq = (t & 7) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(kq + e) * SLD + x] = alpha * v[e];
+        } else {
+            const int xq = (t & 7) * 4, k = t >> 3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[k * SLD + xq + e] = alpha * v[e];
+        }
+    }
+};
+
+// Strip products for the panel step: a 128x128 tile product split four ways
+// so that four groups share it.  ROWS: out is 32 rows x 128 cols (A narrow,
+// B wide; wave w owns columns 32w..32w+31); else 128 rows x 32 cols (A wide,
+// B narrow; wave w owns rows 32w..).  acc += alpha A B over K, computed
+// transposed as in the tile product (lane (h, li), register 4a+b: row li /
+// 32w+li, column 8a+4h+b of the wave's 32x32 block).  lds: 2 * (32*GLD +
+// 32*SLD) floats.
+template <bool ROWS, bool A_KCONTIG, bool B_KCONTIG>
+__device__ __forceinline__ void gemm_strip(f32x16 &acc, const float *A, int64_t lda, const float *B, int64_t ldb,
+                                           int rows, int cols, int K, float alpha, bool vec_ok, float *lds) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, li = lane & 31;
+    constexpr int WST = GK * GLD, NST = GK * SLD;
+    float *wide = lds;                  // [2][WST]
+    float *narrow = lds + 2 * WST;      // [2][NST]
+    const int nch = (K + GK - 1) / GK;
+    if (nch == 0) return;
+    const bool full = (ROWS ? (rows >= 32 && cols >= GT) : (rows >= GT && cols >= 32)) && vec_ok;
+    Chunk<ROWS ? B_KCONTIG : A_KCONTIG> cw;
+    NChunk<ROWS ? A_KCONTIG : B_KCONTIG> cn;
+    auto load = [&](int kb, bool fast) {
+        if (ROWS) {
+            cn.load(A, lda, kb, rows, K, fast);
+            cw.load(B, ldb, kb, cols, K, fast);
+        } else {
+            cw.load(A, lda, kb, rows, K, fast);
+            cn.load(B, ldb, kb, cols, K, fast);
+        }
+    };
+    auto store = [&](int buf) {
+        // alpha goes with A
+        cw.store(wide + buf * WST, ROWS ? 1.f : alpha);
+        cn.store(narrow + buf * NST, ROWS ? alpha : 1.f);
+    };
+    load(0, full && GK <= K);
+    store(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int buf = ch & 1;
+        const bool more = ch + 1 < nch;
+        if (more) load((ch + 1) * GK, full && (ch + 2) * GK <= K);
+        const float *ws = wide + buf * WST;
+        const float *ns = narrow + buf * NST;
+#pragma unroll
+        for (int s = 0; s < GK / 2; ++s) {
+            const int row = 2 * s + h;
+            const float fw = ws[row * GLD + wave * 32 + li];
+            const float fn = ns[row * SLD + li];
+            // D = B^T A^T: the first operand indexes the output columns
+            if (ROWS) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fw, fn, acc, 0, 0, 0);
+            else acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fn, fw, acc, 0, 0, 0);
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+// store of a strip product's accumulator (rows x cols at C, row stride ldc)
+template <bool ROWS>
+__device__ __forceinline__ void store_strip(const f32x16 &acc, float *C, int64_t ldc, int rows, int cols) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, li = lane & 31;
+    const bool vec = ((reinterpret_cast<uintptr_t>(C) & 15) == 0) && (ldc % 4 == 0);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int r = ROWS ? li : wave * 32 + li;
+        const int c = (ROWS ? wave * 32 : 0) + 8 * a + 4 * h;
+        float *dst = C + (int64_t)r * ldc + c;
+        const f32x4 x = {acc[4 * a + 0], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+        if (r < rows) {
+            if (vec && c + 3 < cols) {
+                *(f32x4 *)dst = x;
+            } else {
+                if (c + 0 < cols) dst[0] = x.x;
+                if (c + 1 < cols) dst[1] = x.y;
+                if (c + 2 < cols) dst[2] = x.z;
+                if (c + 3 < cols) dst[3] = x.w;
+            }
+        }
+    }
+}
+
+// Panel step, four groups per 128x128 tile:
+// part A (row blocks below k, 32-row strips): P_i = A_ik Dinv^T -> panel
+// part B (column blocks left of k, 32-column strips): M_kj = -Dinv S_kj, in
+//        place (each group reads and writes only its own columns of S)
 // last group: M_kk = Dinv
 __global__ __launch_bounds__(256) void panel_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
                                                     float *__restrict__ panel, const float *__restrict__ dinv) {
-    __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
+    __shared__ __attribute__((aligned(16))) float lds[2 * GK * (GLD + SLD)];
     const int k0 = k * NB, kb = (int)std::min<int64_t>(NB, d - k0), k1 = k0 + kb;
     const int na = nblk - k - 1;
     const int bid = blockIdx.x;
-    f32x16 acc[4];
-    zero_acc(acc);
-    if (bid < na) {
-        const int row0 = (k + 1 + bid) * NB;
-        const int rows = (int)std::min<int64_t>(NB, d - row0);
-        const float *A = R + (int64_t)row0 * d + k0;          // A(m, k) = R[row0+m][k0+k]
+    f32x16 acc = f32x16{};
+    if (bid < 4 * na) {
+        const int row0 = (k + 1 + bid / 4) * NB + 32 * (bid % 4);
+        const int rows = (int)std::min<int64_t>(32, d - row0);
+        if (rows <= 0) return;                                   // whole group: nothing to do
+        const float *A = R + (int64_t)row0 * d + k0;            // A(m, k) = R[row0+m][k0+k]
         // B(k, n) = Dinv[n][k]: k-contiguous rows of Dinv
-        gemm_tile<true, true>(acc, A, d, dinv, NB, rows, kb, kb, 1.f, aligned16(A, d), lds);
-        store_c(acc, panel + (int64_t)(row0 - k1) * NB, NB, rows, kb);
-    } else if (bid < na + k) {
-        const int col0 = (bid - na) * NB;
-        float *S = R + (int64_t)k0 * d + col0;                 // S(k, n) = R[k0+k][col0+n]
-        gemm_tile<true, false>(acc, dinv, NB, S, d, kb, NB, kb, -1.f, aligned16(S, d), lds);
-        store_c(acc, S, d, kb, NB);
+        gemm_strip<true, true, true>(acc, A, d, dinv, NB, rows, kb, kb, 1.f, aligned16(A, d), lds);
+        store_strip<true>(acc, panel + (int64_t)(row0 - k1) * NB, NB, rows, kb);
+    } else if (bid < 4 * na + 4 * k) {
+        const int col0 = ((bid - 4 * na) / 4) * NB + 32 * ((bid - 4 * na) % 4);
+        float *S = R + (int64_t)k0 * d + col0;                   // S(k, n) = R[k0+k][col0+n]
+        gemm_strip<false, true, false>(acc, dinv, NB, S, d, kb, 32, kb, -1.f, aligned16(S, d), lds);
+        store_strip<false>(acc, S, d, kb, 32);
     } else {
         for (int idx = threadIdx.x; idx < kb * kb; idx += 256) {
             const int i = idx / kb, c = idx % kb;
@@ -482,7 +611,7 @@ hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t
     potrf_kernel<<<1, 256, 0, st>>>(R, d, 0, (int)std::min<int64_t>(NB, d), dbuf[0], info);
     for (int k = 0; k < nblk; ++k) {
         const int na = nblk - k - 1;
-        panel_kernel<<<na + k + 1, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1]);
+        panel_kernel<<<4 * (na + k) + 1, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1]);
         const int nup = nblk * (nblk + 1) / 2 - (k + 1) * (k + 2) / 2;
         if (nup > 0)
             update_kernel<<<nup, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1], dbuf[(k + 1) & 1], info);
