@@ -450,9 +450,29 @@ __global__ __launch_bounds__(256) void panel_kernel(float *__restrict__ R, int64
         gemm_strip<false, true, false>(acc, dinv, NB, S, d, kb, 32, kb, -1.f, aligned16(S, d), lds);
         store_strip<false>(acc, S, d, kb, 32);
     } else {
-        for (int idx = threadIdx.x; idx < kb * kb; idx += 256) {
-            const int i = idx / kb, c = idx % kb;
-            R[(int64_t)(k0 + i) * d + k0 + c] = dinv[i * NB + c];
+        // M_kk = Dinv (kb x kb, upper part zero): thread t copies 4-column
+        // group t % 32 of rows t / 32 + 8q, all loads before any store
+        const int t = threadIdx.x, c4 = 4 * (t & 31);
+        const bool vec = (d % 4 == 0);
+        f32x4 v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = (t >> 5) + 8 * q;
+            v[q] = (i < kb) ? *(const f32x4 *)(dinv + i * NB + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = (t >> 5) + 8 * q;
+            if (i >= kb) continue;
+            float *dst = R + (int64_t)(k0 + i) * d + k0 + c4;
+            if (vec && c4 + 3 < kb) {
+                *(f32x4 *)dst = v[q];
+            } else {
+                if (c4 + 0 < kb) dst[0] = v[q].x;
+                if (c4 + 1 < kb) dst[1] = v[q].y;
+                if (c4 + 2 < kb) dst[2] = v[q].z;
+                if (c4 + 3 < kb) dst[3] = v[q].w;
+            }
         }
     }
 }
