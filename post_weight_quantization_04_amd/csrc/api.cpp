@@ -345,37 +345,38 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
     qa.bits = bits;
     qa.group = L.group;
     qa.block = L.block_int;
-    // Errors of the blocks since the last far update are stacked in E (block
-    // t of the batch at rows t*B..).  Each block's in-block kernel first
-    // applies all of them to its own columns (the near update), and every
-    // FAR_BLOCKS blocks one product applies them to every column beyond.  A
-    // group wider than a block takes its parameters from all its columns at
-    // its start, so the pending errors are also flushed to every column
+    // Blocks go in batches of FAR_BLOCKS; the errors of a batch's blocks are
+    // stacked in E (block t of the batch at rows t*B..).  One in-block launch
+    // takes the whole batch, each block first applying the batch's earlier
+    // errors to its own columns (the near update); then one product applies
+    // all of them to every column beyond.  A group wider than a block takes
+    // its parameters from all its columns at its start, so a batch also ends
     // before such a group begins.
     const int64_t B = L.block_int;
-    int64_t pend0 = 0;   // first column of the oldest pending block
-    int slot = 0;
-    for (int64_t b = 0; b < d_in; b += B) {
-        const int64_t e = std::min<int64_t>(b + B, d_in);
+    for (int64_t pend0 = 0; pend0 < d_in;) {
+        // one batch: up to FAR_BLOCKS blocks, ending early after a block whose
+        // end starts a group wider than a block
+        int nblk = 0;
+        int64_t e = pend0;
+        while (nblk < gptq::FAR_BLOCKS && e < d_in) {
+            e = std::min<int64_t>(e + B, d_in);
+            ++nblk;
+            if (L.group > B && e % L.group == 0) break;
+        }
         {
             StageTimer t(5, st);
             gptq::QuantArgs qb = qa;
-            qb.E = w.E + (size_t)slot * B * d_out;
+            qb.E = w.E;
             qb.En = w.E;
             qb.near_row0 = pend0;
-            qb.near_k = (int)(b - pend0);
-            HIPCHECK(gptq::quant_block_launch(qb, b, e, st));
+            HIPCHECK(gptq::quant_block_launch(qb, pend0, nblk, B, st));
         }
         if (e >= d_in) break;
-        const bool wide_group_next = L.group > B && e % L.group == 0;
-        if (slot + 1 == gptq::FAR_BLOCKS || wide_group_next) {
+        {
             StageTimer t(6, st);
             HIPCHECK(gptq::trail_launch(qa, pend0, e - pend0, e, d_in, st));
-            pend0 = e;
-            slot = 0;
-        } else {
-            ++slot;
         }
+        pend0 = e;
     }
     {
         StageTimer t(7, st);

@@ -76,10 +76,10 @@ struct QuantArgs {
     const float *U;        // [d_in][d_in] upper factor (row-major, upper part valid)
     const float *ud;       // [d_in] U diagonal
     const float *uinv;     // [d_in] 1 / U diagonal
-    float *E;              // [K][d_out] block errors (quant_block writes rows 0..B-1 of the slot it is given)
-    const float *En;       // [near_k][d_out] errors of the pending blocks (quant_block reads them)
+    float *E;              // [K][d_out] pending blocks' errors (block at column b: rows b - near_row0 ..)
+    const float *En;       // the same errors as read for the near update (rows < b - near_row0)
     int64_t near_row0;     // first column of the pending blocks (their rows of U)
-    int near_k;            // pending columns; quant_block first applies them to its own columns
+    int near_k;            // pending columns before the block being quantized (set per block)
     uint8_t *codes;        // [d_in][d_out]
     float *scales;         // [G][d_out]
     float *zeros;          // [G][d_out]
@@ -87,7 +87,8 @@ struct QuantArgs {
     int bits, group, block;   // group: effective group size (d_in when one group)
 };
 size_t quant_lds_bytes(int block);
-hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st);
+// blocks [b0 + t*B, min(b0 + (t+1)*B, d_in)) for t < nblocks, one launch
+hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64_t B, hipStream_t st);
 // Blocks whose errors are applied to the far columns together (two-level
 // lazy update): each block's in-block kernel first takes the pending blocks'
 // errors on its own columns, and every FAR_BLOCKS blocks one product applies

@@ -132,8 +132,11 @@ __device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, cons
     (qstep<S, RAGGED>(w, myq, myE, cx, Q, uu, sv, ui, su), ...);
 }
 
-// One launch per block [b, e).  Grid: ceil(d_out / 16) groups of 256 threads.
-__global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, int e) {
+// Block [b, e) for this group's 16 rows.  a.E is the block's error slot and
+// a.near_k the pending columns before b.  Q carries a group's parameters
+// from one block to the next; first: b is the launch's first block (a group
+// that began before it has its parameters read back from scales/zeros).
+__device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e, Quantizer &Q, bool first) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int nb = e - b;
     const int Bp = roundup16(nb);
@@ -294,8 +297,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
 
     const float maxq = (float)((1 << a.bits) - 1);
     const int g = a.group;
-    Quantizer Q = reuse_quantizer(1.f, 0.f, maxq);
-    if (b % g != 0) {
+    if (first && b % g != 0) {
         // the current group began in an earlier block: reuse its parameters
         const int64_t gi = b / g;
         Q = reuse_quantizer(row_ok ? a.scales[gi * d_out + row] : 1.f, row_ok ? a.zeros[gi * d_out + row] : 0.f,
@@ -418,6 +420,30 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b, in
     }
 }
 
+// BATCH: one launch takes nblocks blocks of width B from b0 (the blocks
+// between two far updates): each group takes its 16 rows through all of them.
+// Nothing crosses groups within a batch (a block's near update uses this
+// group's own earlier errors), so the blocks need no grid-wide
+// synchronization.  The loop keeps the kernel's arguments live across the
+// whole body (≈ 340 VGPRs, one group per SIMD set), so it is used when the grid
+// fits in one group per CU; otherwise one launch per block (nblocks = 1).
+// a.E / a.En: the batch's error slots ([k][d_out], block t at rows t*B);
+// a.near_row0: the batch's first column.
+// Grid: ceil(d_out / 16) groups of 256 threads.
+template <bool BATCH>
+__global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b0, int nblocks, int B) {
+    Quantizer Q = reuse_quantizer(1.f, 0.f, (float)((1 << a.bits) - 1));
+    for (int t = 0; t < (BATCH ? nblocks : 1); ++t) {
+        QuantArgs ab = a;
+        const int b = b0 + t * B;
+        const int e = (int)std::min<int64_t>(b + B, ab.d_in);
+        ab.E = ab.E + (int64_t)(b - ab.near_row0) * ab.d_out;
+        ab.near_k = b - (int)ab.near_row0;
+        quant_one_block(ab, b, e, Q, t == 0);
+        __syncthreads();   // the next block restages the LDS
+    }
+}
+
 }  // namespace
 
 size_t quant_lds_bytes(int block) {
@@ -425,19 +451,44 @@ size_t quant_lds_bytes(int block) {
     return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp) + 2 * (size_t)Bp + (size_t)QROWS * ELD);
 }
 
-hipError_t quant_block_launch(const QuantArgs &a, int64_t b, int64_t e, hipStream_t st) {
+int quant_cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            cached = cus;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
+hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64_t B, hipStream_t st) {
     static bool attr_done = false;
     if (!attr_done) {
-        hipError_t err = hipFuncSetAttribute((const void *)quant_block_kernel,
+        hipError_t err = hipFuncSetAttribute((const void *)quant_block_kernel<true>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (err == hipSuccess)
+            err = hipFuncSetAttribute((const void *)quant_block_kernel<false>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (err != hipSuccess) return err;
         attr_done = true;
     }
-    if (e - b < 1 || e - b > 256) return hipErrorInvalidValue;   // the kernel stages at most 256 columns
-    const size_t lds = quant_lds_bytes((int)(e - b));
+    if (B < 1 || B > 256 || nblocks < 1 || b0 + (nblocks - 1) * B >= a.d_in || b0 < a.near_row0)
+        return hipErrorInvalidValue;   // the kernel stages at most 256 columns per block
+    const size_t lds = quant_lds_bytes((int)std::min<int64_t>(B, a.d_in - b0));   // the widest block is the first
     const unsigned grid = (unsigned)cdiv(a.d_out, QROWS);
-    quant_block_kernel<<<grid, 256, lds, st>>>(a, (int)b, (int)e);
-    return hipGetLastError();
+    if ((int64_t)grid <= quant_cu_count()) {
+        quant_block_kernel<true><<<grid, 256, lds, st>>>(a, (int)b0, nblocks, (int)B);
+        return hipGetLastError();
+    }
+    for (int t = 0; t < nblocks; ++t) {
+        quant_block_kernel<false><<<grid, 256, lds, st>>>(a, (int)(b0 + t * B), 1, (int)B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gptq

@@ -195,6 +195,7 @@ LAYER_CASES = [
     ("up_proj", 310, 33, 250, 1500, 3, 16, 80, True),          # odd block, group 16
     ("q_proj", 311, 40, 1536, 3000, 4, 512, 512, False),       # groups of 512 over two 256-column internal blocks
     ("down_proj", 312, 24, 2304, 3000, 4, 768, 768, True),     # groups of 768 over three internal blocks
+    ("q_proj", 314, 4200, 384, 2048, 4, 128, 128, False),      # more row groups than CUs: one launch per block
 ]
 
 
