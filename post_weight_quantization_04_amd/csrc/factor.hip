@@ -183,22 +183,37 @@ __device__ __forceinline__ void blk_store(const f32x16 &acc, float *F, int r0, i
 }
 
 // F = the kb x kb block at src (row stride ld; lower triangle read), identity
-// past kb.  Loads are issued in batches so that many are in flight per thread.
+// past kb.  Thread t takes 4-column group t % 32 of rows t / 32 + 8q, all of
+// its loads issued before any store.
 __device__ __forceinline__ void potrf_block_load(const float *__restrict__ src, int64_t ld, int kb, float *F) {
-    const int tid = threadIdx.x;
+    const int t = threadIdx.x, c4 = 4 * (t & 31);
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && (ld % 4 == 0) && (kb % 4 == 0);
+    f32x4 v[16];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        float v[32];
-#pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int idx = tid + 256 * (32 * half + q);
-            const int i = idx >> 7, c = idx & (NB - 1);
-            v[q] = (i < kb && c < kb && c <= i) ? src[(int64_t)i * ld + c] : (i == c ? 1.f : 0.f);
+    for (int q = 0; q < 16; ++q) {
+        const int i = (t >> 5) + 8 * q;
+        const float *p = src + (int64_t)i * ld + c4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (i < kb && c4 <= i) {
+            if (vec) {
+                x = *(const f32x4 *)p;
+            } else {
+                if (c4 + 0 < kb) x.x = p[0];
+                if (c4 + 1 < kb) x.y = p[1];
+                if (c4 + 2 < kb) x.z = p[2];
+                if (c4 + 3 < kb) x.w = p[3];
+            }
         }
+        v[q] = x;
+    }
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int idx = tid + 256 * (32 * half + q);
-            F[(idx >> 7) * FLD + (idx & (NB - 1))] = v[q];
+    for (int q = 0; q < 16; ++q) {
+        const int i = (t >> 5) + 8 * q;
+        const float e[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c4 + u;
+            F[i * FLD + c] = (i < kb && c < kb && c <= i) ? e[u] : (i == c ? 1.f : 0.f);
         }
     }
 }
@@ -287,7 +302,7 @@ __device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base,
     }
 }
 
-__global__ __launch_bounds__(256) void potrf_kernel(const float *__restrict__ R, int64_t d, int k0, int kb,
+__global__ __launch_bounds__(256, 2) void potrf_kernel(const float *__restrict__ R, int64_t d, int k0, int kb,
                                                     float *__restrict__ dinv, int32_t *__restrict__ info) {
     __shared__ __attribute__((aligned(16))) float F[NB * FLD];
     __shared__ __attribute__((aligned(16))) float bc[64];

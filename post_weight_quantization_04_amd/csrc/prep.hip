@@ -71,7 +71,11 @@ __global__ void zero_i32_kernel(int32_t *__restrict__ p, int64_t n) {
     if (i < n) p[i] = 0;
 }
 
-// R[a][b] = H[p(a)][p(b)] (+ lambda if a == b), p(a) = perm[d-1-a]; one row per block.
+constexpr int GATHER_UNROLL = 8;   // elements per thread in flight
+
+// R[a][b] = H[p(a)][p(b)] (+ lambda if a == b), p(a) = perm[d-1-a]; one row per
+// block, eight elements per thread at a time (index loads, then the gathered
+// loads, then the stores).
 __global__ __launch_bounds__(256) void gather_h_kernel(const float *__restrict__ H, const int32_t *__restrict__ perm,
                                                        const float *__restrict__ lam, int64_t d,
                                                        float *__restrict__ R) {
@@ -80,10 +84,21 @@ __global__ __launch_bounds__(256) void gather_h_kernel(const float *__restrict__
     const float l = lam[0];
     const float *hrow = H + pa * d;
     float *rrow = R + a * d;
-    for (int64_t b = threadIdx.x; b < d; b += 256) {
-        float v = hrow[perm[d - 1 - b]];
-        if (b == a) v += l;
-        rrow[b] = v;
+    for (int64_t b0 = threadIdx.x; b0 < d; b0 += 256 * GATHER_UNROLL) {
+        int32_t pb[GATHER_UNROLL];
+        float v[GATHER_UNROLL];
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) {
+            const int64_t b = b0 + 256 * u;
+            pb[u] = (b < d) ? perm[d - 1 - b] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) v[u] = hrow[pb[u]];
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) {
+            const int64_t b = b0 + 256 * u;
+            if (b < d) rrow[b] = (b == a) ? v[u] + l : v[u];
+        }
     }
 }
 
@@ -91,16 +106,28 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void gather_w_kernel(const void *__restrict__ W, const int32_t *__restrict__ perm,
                                                        int64_t d_in, float *__restrict__ Wp) {
     const int64_t r = blockIdx.x;
-    for (int64_t k = threadIdx.x; k < d_in; k += 256) {
-        const int64_t c = perm[k];
-        float v;
-        if (BF16) {
-            const unsigned short b = ((const unsigned short *)W)[r * d_in + c];
-            v = __uint_as_float((unsigned)b << 16);
-        } else {
-            v = ((const float *)W)[r * d_in + c];
+    for (int64_t k0 = threadIdx.x; k0 < d_in; k0 += 256 * GATHER_UNROLL) {
+        int32_t c[GATHER_UNROLL];
+        float v[GATHER_UNROLL];
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) {
+            const int64_t k = k0 + 256 * u;
+            c[u] = (k < d_in) ? perm[k] : 0;
         }
-        Wp[r * d_in + k] = v;
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) {
+            if (BF16) {
+                const unsigned short b = ((const unsigned short *)W)[r * d_in + c[u]];
+                v[u] = __uint_as_float((unsigned)b << 16);
+            } else {
+                v[u] = ((const float *)W)[r * d_in + c[u]];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) {
+            const int64_t k = k0 + 256 * u;
+            if (k < d_in) Wp[r * d_in + k] = v[u];
+        }
     }
 }
 
