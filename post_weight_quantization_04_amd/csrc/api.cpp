@@ -158,7 +158,7 @@ Workspace layout(const LayerShape &L, char *base) {
     w.uinv = (float *)take(sizeof(float) * d);
     w.rank = (int32_t *)take(sizeof(int32_t) * d);
     w.lam = (float *)take(sizeof(float));
-    w.info = (int32_t *)take(sizeof(int32_t));
+    w.info = (int32_t *)take(2 * sizeof(int32_t));   // pivot flag, step counter
     w.bytes = off;
     return w;
 }
@@ -166,7 +166,7 @@ Workspace layout(const LayerShape &L, char *base) {
 // damping, order, gathers, factorization, status sync, flip.
 gptq_status run_factor(const float *H, int64_t d, float damp, int act_order, int32_t *perm, Workspace &w,
                        hipStream_t st) {
-    HIPCHECK(hipMemsetAsync(w.info, 0, sizeof(int32_t), st));
+    HIPCHECK(hipMemsetAsync(w.info, 0, 2 * sizeof(int32_t), st));
     {
         StageTimer t(2, st);
         HIPCHECK(gptq::prep_diag_lambda(H, d, damp, w.dg, w.lam, st));
@@ -188,6 +188,8 @@ gptq_status read_pivot_flag(const Workspace &w, hipStream_t st) {
     int32_t info = 0;
     HIPCHECK(hipMemcpyAsync(&info, w.info, sizeof(int32_t), hipMemcpyDeviceToHost, st));
     HIPCHECK(hipStreamSynchronize(st));
+    if (info == gptq::FACTOR_SYNC_TIMEOUT)
+        return fail(GPTQ_EHIP, "factorization: the look-ahead gave up waiting for the diagonal update");
     if (info != 0)
         return fail(GPTQ_ENOTSPD, "damped Hessian is not positive definite (pivot %lld of the reversed order)",
                     (long long)info - 1);

@@ -60,6 +60,10 @@ hipError_t prep_gather_w(const void *W, int is_bf16, const int32_t *perm, int64_
 constexpr int FACT_NB = 128;
 // panel: d * FACT_NB floats; dinv: 2 * FACT_NB^2 floats (the inverse of the
 // current diagonal block and, written ahead by the fused update, the next one).
+// info: 2 int32, zero on entry.  info[0] receives the first bad pivot + 1, or
+// FACTOR_SYNC_TIMEOUT if the look-ahead's wait for its helpers gave up;
+// info[1] counts the helpers' completed diagonal-tile updates.
+constexpr int32_t FACTOR_SYNC_TIMEOUT = -1;
 hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t *info,
                          hipStream_t st);
 // U[k][j] = M[d-1-k][d-1-j] for k < j (in place, upper triangle);

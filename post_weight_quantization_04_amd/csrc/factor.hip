@@ -21,8 +21,10 @@
 //              j == k: S_ik  = P_i Dinv_k     (first term of the inverse sum)
 //              j <  k: S_ij += P_i M_kj       (inverse accumulation)
 //            where S_ij = sum_{m=j}^{i-1} L_im M_mj occupies the strictly lower
-//            blocks already consumed by the Cholesky.  Work group 0 takes tile
-//            (k+1, k+1) and then factors it (potrf of the next step).
+//            blocks already consumed by the Cholesky.  Work groups 1..3
+//            update the next diagonal tile (k+1, k+1), one 64x64 quadrant
+//            each, and count their completion in info[1]; work group 0 waits
+//            for that count, then factors the tile (potrf of the next step).
 // Dinv alternates between two buffers by step parity because the fused
 // potrf writes the next step's while the rest of the kernel reads this one.
 // The tile products run on fp32 MFMA (v_mfma_f32_32x32x2_f32).
@@ -492,95 +494,179 @@ __global__ __launch_bounds__(256) void panel_kernel(float *__restrict__ R, int64
     }
 }
 
-// acc -= P P^T for the 128x128 diagonal tile, P (rows x kb) at p with row
-// stride NB (16-byte aligned rows).  F: NB * FLD floats of LDS.  Accumulator
-// layout as tile_rc: wave (wr, wc) owns the 64x64 quadrant, 2x2 32x32 tiles.
-__device__ __forceinline__ void diag_tile_update(f32x16 (&acc)[4], const float *__restrict__ p, int rows, int kb,
-                                                 float *F) {
+// Step counter shared by the diagonal-update helpers and the look-ahead
+// factorization (info[1], zero at the start of each factorization): after
+// step k's update kernel it reads 3 (k + 1).  The waiting thread polls with
+// device-scope atomic loads and a short sleep, at most STEP_SPIN_LIMIT times;
+// on time-out it records FACTOR_SYNC_TIMEOUT in info[0] (unless a pivot error
+// is already there) and goes on, so every group finishes.  The helpers are
+// dispatched right after the waiting group and wait for nothing.
+constexpr int STEP_SPIN_LIMIT = 1 << 20;
+
+__device__ __forceinline__ void wait_count(int32_t *cnt, int target, int32_t *info) {
+    if (threadIdx.x == 0) {
+        int v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int it = 0; v < target && it < STEP_SPIN_LIMIT; ++it) {
+            __builtin_amdgcn_s_sleep(2);
+            v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (v < target) atomicCAS(info, 0, FACTOR_SYNC_TIMEOUT);
+        // what the helpers wrote before their release is visible after this
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void signal_count(int32_t *cnt) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this wave's stores
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Helper q of step k: quadrant (qa, qb) = (0,0), (1,0), (1,1) of the next
+// diagonal tile (k+1, k+1) of R takes C -= P_a P_b^T in place, with P the
+// panel rows of block k+1 (rows x kb, k-contiguous, at the panel's start).
+// The P rows of the two 64-row halves are staged in LDS ([row][k], stride
+// FLD); wave w takes the 32x32 sub-block (w/2, w%2) of the quadrant (none
+// above the diagonal of a diagonal quadrant) on fp32 MFMA, computed
+// transposed (lane (h, li), register 4a+b: row li, column 8a+4h+b).
+__device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, int n0, int rows, int kb, int q,
+                                              const float *__restrict__ P, float *lds) {
+    const int qa = (q >= 1) ? 1 : 0, qb = (q == 2) ? 1 : 0;
+    const int ra = 64 * qa, rb = 64 * qb;
+    if (ra >= rows) return;   // the block has no such quadrant
     const int tid = threadIdx.x;
-    // stage P: 128 rows x 32 float4 groups, 16 groups per thread, zero past rows/kb
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    // stage P rows [ra, ra+64) as operand 0 and [rb, rb+64) as operand 1
+    // (the same rows for a diagonal quadrant), zero past rows / kb
+    const int nop = (qa == qb) ? 1 : 2;
+    for (int op = 0; op < nop; ++op) {
+        const int r0 = op ? rb : ra;
         f32x4 v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int f = tid + 256 * (8 * half + q);
-            const int m = f >> 5, k4 = 4 * (f & 31);
-            v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (m < rows) {
+        for (int u = 0; u < 8; ++u) {
+            const int f = tid + 256 * u;                 // 64 rows x 32 groups
+            const int r = f >> 5, k4 = 4 * (f & 31);
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (r0 + r < rows) {
+                const float *src = P + (int64_t)(r0 + r) * NB + k4;
                 if (k4 + 3 < kb) {
-                    v[q] = *(const f32x4 *)(p + (int64_t)m * NB + k4);
+                    x = *(const f32x4 *)src;
                 } else {
-                    if (k4 + 0 < kb) v[q].x = p[(int64_t)m * NB + k4 + 0];
-                    if (k4 + 1 < kb) v[q].y = p[(int64_t)m * NB + k4 + 1];
-                    if (k4 + 2 < kb) v[q].z = p[(int64_t)m * NB + k4 + 2];
+                    if (k4 + 0 < kb) x.x = src[0];
+                    if (k4 + 1 < kb) x.y = src[1];
+                    if (k4 + 2 < kb) x.z = src[2];
                 }
             }
+            v[u] = x;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int f = tid + 256 * (8 * half + q);
-            const int m = f >> 5, k4 = 4 * (f & 31);
-            float *dst = F + m * FLD + k4;
-            dst[0] = v[q].x;
-            dst[1] = v[q].y;
-            dst[2] = v[q].z;
-            dst[3] = v[q].w;
+        for (int u = 0; u < 8; ++u) {
+            const int f = tid + 256 * u;
+            const int r = f >> 5, k4 = 4 * (f & 31);
+            float *dst = lds + (op * 64 + r) * FLD + k4;
+            dst[0] = v[u].x;
+            dst[1] = v[u].y;
+            dst[2] = v[u].z;
+            dst[3] = v[u].w;
         }
     }
     __syncthreads();
-    const int wave = tid >> 6, lane = tid & 63;
-    const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
-    const float *Ar = F + (wr * 64 + li) * FLD;
-    const float *Br = F + (wc * 64 + li) * FLD;
+    const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, li = lane & 31;
+    const int sa = wave >> 1, sb = wave & 1;
+    if (qa == qb && sa < sb) return;                       // above the diagonal: not needed
+    const int r = ra + 32 * sa + li;                       // this lane's row of the tile
+    const int cb = rb + 32 * sb;                           // the sub-block's first column
+    const float *Ar = lds + (32 * sa + li) * FLD;                        // P row ra + 32 sa + li
+    const float *Br = lds + ((nop - 1) * 64 + 32 * sb + li) * FLD;      // P row rb + 32 sb + li
+    float *Crow = R + (int64_t)(n0 + r) * d + n0;
+    f32x16 acc;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int c = cb + 8 * a + 4 * h;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (r < rows) {
+            if (c + 3 < rows) {
+                x = *(const f32x4 *)(Crow + c);
+            } else {
+                if (c + 0 < rows) x.x = Crow[c + 0];
+                if (c + 1 < rows) x.y = Crow[c + 1];
+                if (c + 2 < rows) x.z = Crow[c + 2];
+            }
+        }
+        acc[4 * a + 0] = x.x;
+        acc[4 * a + 1] = x.y;
+        acc[4 * a + 2] = x.z;
+        acc[4 * a + 3] = x.w;
+    }
 #pragma unroll 8
     for (int kk = 0; kk < NB; kk += 2) {
-        const int k = kk + h;
-        const float a0 = -Ar[k], a1 = -Ar[32 * FLD + k];
-        const float b0 = Br[k], b1 = Br[32 * FLD + k];
-        // transposed products, as in the tile product (accumulator layout of tile_rc)
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[3], 0, 0, 0);
+        const int kx = kk + h;
+        // D[n][m] += sum_k B(k, n) A(k, m) with A = -P_a, B = P_b
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Br[kx], -Ar[kx], acc, 0, 0, 0);
     }
-    __syncthreads();   // F is reused by the caller
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int c = cb + 8 * a + 4 * h;
+        const f32x4 x = {acc[4 * a + 0], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+        if (r < rows) {
+            if (c + 3 < rows) {
+                *(f32x4 *)(Crow + c) = x;
+            } else {
+                if (c + 0 < rows) Crow[c + 0] = x.x;
+                if (c + 1 < rows) Crow[c + 1] = x.y;
+                if (c + 2 < rows) Crow[c + 2] = x.z;
+            }
+        }
+    }
 }
 
-// Update of step k plus look-ahead factorization of block k+1 (work group 0).
+// Update of step k plus the look-ahead factorization of block k+1.
+//   group 0     : waits for the three helpers, then loads the next diagonal
+//                 tile (k+1, k+1) from R and factors it (look-ahead), writing
+//                 Dinv_{k+1} to dinv_next.
+//   groups 1..3 : the next diagonal tile's update, one 64x64 quadrant each.
+//   groups 4..  : every other tile in rows > k, as for the tile product:
+//                 (k+1, 0..k) first, then the rows below in order.
 __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
                                                      const float *__restrict__ panel,
                                                      const float *__restrict__ dinv_k,
                                                      float *__restrict__ dinv_next, int32_t *__restrict__ info) {
     __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
     __shared__ __attribute__((aligned(16))) float bc[64];
-    // work group 0 -> tile (k+1, k+1); 1..k+1 -> (k+1, 0..k); the rest in order
-    const int base = (k + 1) * (k + 2) / 2;
-    int i, j;
-    if (blockIdx.x == 0) {
-        i = k + 1;
-        j = k + 1;
-    } else if ((int)blockIdx.x <= k + 1) {
-        i = k + 1;
-        j = blockIdx.x - 1;
-    } else {
-        tile_coords(base + blockIdx.x, i, j);
-    }
     const int k0 = k * NB, kb = (int)std::min<int64_t>(NB, d - k0), k1 = k0 + kb;
+    const int b = blockIdx.x;
+    if (b < 4) {
+        const int n0 = (k + 1) * NB;
+        const int rows = (int)std::min<int64_t>(NB, d - n0);
+        if (b > 0) {
+            diag_quadrant(R, d, n0, rows, kb, b - 1, panel + (int64_t)(n0 - k1) * NB, lds);
+            signal_count(info + 1);
+            return;
+        }
+        wait_count(info + 1, 3 * (k + 1), info);
+        float *F = lds;
+        potrf_block_load(R + (int64_t)n0 * d + n0, d, rows, F);
+        __syncthreads();
+        potrf_block_lds(F, rows, n0, info, bc);
+        potrf_block_store(F, rows, dinv_next);
+        return;
+    }
+    // the tile product: (k+1, 0..k), then the rows below in order
+    const int bb = b - 3;
+    int i, j;
+    if (bb <= k + 1) {
+        i = k + 1;
+        j = bb - 1;
+    } else {
+        tile_coords((k + 1) * (k + 2) / 2 + bb, i, j);
+    }
     const int row0 = i * NB, col0 = j * NB;
     const int rows = (int)std::min<int64_t>(NB, d - row0);
     const int cols = (int)std::min<int64_t>(NB, d - col0);
     float *C = R + (int64_t)row0 * d + col0;
     const float *A = panel + (int64_t)(row0 - k1) * NB;       // A(m, k) = P[row0+m][k]
     f32x16 acc[4];
-    if (blockIdx.x == 0) {
-        // The next diagonal tile: C - P P^T with P = the panel rows of block
-        // k+1 (rows x kb, k-contiguous).  P is staged once into LDS ([m][k],
-        // row stride FLD) and feeds both operands; all of its loads and the
-        // tile's own go out before any is consumed.
-        load_c(acc, C, d, rows, cols);
-        diag_tile_update(acc, A, rows, kb, lds);
-    } else if (j == k) {
+    if (j == k) {
         zero_acc(acc);
         // B(k, n) = Dinv[k][n]: n-contiguous
         gemm_tile<true, false>(acc, A, NB, dinv_k, NB, rows, cols, kb, 1.f, true, lds);
@@ -593,30 +679,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
         const float *B = panel + (int64_t)(col0 - k1) * NB;    // B(k, n) = P[col0+n][k]
         gemm_tile<true, true>(acc, A, NB, B, NB, rows, cols, kb, -1.f, true, lds);
     }
-    if (blockIdx.x != 0) {
-        store_c(acc, C, d, rows, cols);
-        return;
-    }
-    // Look-ahead: the tile just updated is the next diagonal block.  Nothing
-    // else reads it from R (the panel step overwrites it with its inverse),
-    // so it goes from the accumulators straight into LDS, identity past kb.
-    // gemm_tile ended on a barrier: the staging area is free.
-    float *F = lds;
-#pragma unroll
-    for (int ma = 0; ma < 2; ++ma)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    int r, c;
-                    tile_rc(ma, mb, a, b, r, c);
-                    F[r * FLD + c] = (r < rows && c < cols) ? acc[ma * 2 + mb][4 * a + b] : (r == c ? 1.f : 0.f);
-                }
-    __syncthreads();
-    potrf_block_lds(F, rows, row0, info, bc);
-    potrf_block_store(F, rows, dinv_next);
+    store_c(acc, C, d, rows, cols);
 }
 
 __global__ void flip_kernel(float *__restrict__ R, int64_t d, float *__restrict__ ud) {
@@ -647,9 +710,11 @@ hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t
     for (int k = 0; k < nblk; ++k) {
         const int na = nblk - k - 1;
         panel_kernel<<<4 * (na + k) + 1, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1]);
+        // tiles in rows > k besides the next diagonal one, plus the look-ahead
+        // group and its three helpers
         const int nup = nblk * (nblk + 1) / 2 - (k + 1) * (k + 2) / 2;
         if (nup > 0)
-            update_kernel<<<nup, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1], dbuf[(k + 1) & 1], info);
+            update_kernel<<<nup + 3, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1], dbuf[(k + 1) & 1], info);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
