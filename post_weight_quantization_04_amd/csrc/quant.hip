@@ -25,6 +25,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 namespace gptq {
@@ -48,9 +49,11 @@ __host__ __device__ inline int usize(int Bp) { return uoff(Bp, Bp); }
 __device__ __forceinline__ int uidx(int i, int j, int Bp) { return uoff(i, Bp) + j - 4 * (i >> 2); }
 constexpr int ELD = CH + 1;   // row stride of the chunk's error tile in LDS
 
+// lane S of each 16-lane DPP row to the whole row (every lane is written, so
+// no old value is needed)
 template <int S>
 __device__ __forceinline__ float bcast16(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + S, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + S, 0xF, 0xF, true));
 }
 
 // lo = -z and hi = maxq - z bound the code relative to the zero point:
@@ -101,35 +104,48 @@ __device__ __forceinline__ void minmax16(float &mn, float &mx) {
     mx = fmaxf(mx, dpp_f<0xB1>(mx));
 }
 
-struct StepCtx {
-    int c0, c, nb;
-};
-
-// Column S of the chunk: every lane of the row quantizes the broadcast value
-// x and applies the error to its own column c:
+// Column S of the chunk (i = c0 + S): every lane of the row quantizes the
+// broadcast value x and applies the error to its own column c:
 //   w_c -= E U_{i,c} = w_c - x U_{i,c}/U_ii + r s U_{i,c}/U_ii
 // with uu[S] = U_{i,c}/U_ii and sv[S] = s U_{i,c}/U_ii (both 0 for c <= S),
 // so that only the code (round, clamp) and one fma stay on the chain from
-// one column to the next.  The error itself, (x - s r)/U_ii, is only output.
+// one column to the next.  Lane S's own value is never changed again from
+// step S on (its coefficients are zero there), so its code and error are
+// taken from its final value after the chunk, off the chain.
 template <int S, bool RAGGED>
-__device__ __forceinline__ void qstep(float &w, float &myq, float &myE, const StepCtx &cx, const Quantizer &Q,
-                                      const float (&uu)[CH], const float (&sv)[CH], const float (&ui)[CH],
-                                      const float (&su)[CH]) {
-    if (RAGGED && cx.c0 + S >= cx.nb) return;       // uniform: ragged last chunk
+__device__ __forceinline__ void qstep(float &w, int c0, int nb, const Quantizer &Q, const float (&uu)[CH],
+                                      const float (&sv)[CH]) {
+    if (RAGGED && c0 + S >= nb) return;       // uniform: ragged last chunk
     const float x = bcast16<S>(w);
     const float r = __builtin_amdgcn_fmed3f(rintf(x * Q.inv_s), Q.lo, Q.hi);   // code - z
     const float t = fmaf(-x, uu[S], w);
-    const float err = fmaf(-su[S], r, x * ui[S]);                              // (w - s (q - z)) / U_kk
-    myq = (cx.c == S) ? r + Q.z : myq;
-    myE = (cx.c == S) ? err : myE;
     w = fmaf(r, sv[S], t);
 }
 
 template <bool RAGGED, int... S>
-__device__ __forceinline__ void run_chunk(float &w, float &myq, float &myE, const StepCtx &cx, const Quantizer &Q,
-                                          const float (&uu)[CH], const float (&sv)[CH], const float (&ui)[CH],
-                                          const float (&su)[CH], std::integer_sequence<int, S...>) {
-    (qstep<S, RAGGED>(w, myq, myE, cx, Q, uu, sv, ui, su), ...);
+__device__ __forceinline__ void run_chunk(float &w, int c0, int nb, const Quantizer &Q, const float (&uu)[CH],
+                                          const float (&sv)[CH], std::integer_sequence<int, S...>) {
+    (qstep<S, RAGGED>(w, c0, nb, Q, uu, sv), ...);
+}
+
+// u[S] = U_{c0+S, c0+c} for c > S and 0 for c <= S (the packed block holds
+// zeros on and below the diagonal, and max(c, S) reads the diagonal), and
+// ui[S] = 1/U_{c0+S, c0+S}, for the 16 rows of chunk c0.  c0 and Bp are
+// multiples of 16, so rows c0..c0+15 all exist (past nb they hold zeros) and
+// max(c, S) stays inside row c0+S's packed range, which starts at column
+// c0 + 4 floor(S/4).
+__device__ __forceinline__ void load_coef(const float *Ul, const float *uil, int c0, int Bp, int cl, float (&u)[CH],
+                                          float (&ui)[CH]) {
+#pragma unroll
+    for (int q = 0; q < CH / 4; ++q) {
+        const f32x4 x = *(const f32x4 *)(uil + c0 + 4 * q);
+        ui[4 * q + 0] = x.x;
+        ui[4 * q + 1] = x.y;
+        ui[4 * q + 2] = x.z;
+        ui[4 * q + 3] = x.w;
+    }
+#pragma unroll
+    for (int S = 0; S < CH; ++S) u[S] = Ul[uidx(c0 + S, c0, Bp) + max(cl, S)];
 }
 
 // Block [b, e) for this group's 16 rows.  a.E is the block's error slot and
@@ -144,7 +160,7 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
     float *Wl = lds;                       // [16][LW]
     float *Ul = lds + QROWS * LW;          // packed upper U block
     float *uil = Ul + usize(Bp);           // 1/U_kk of the block
-    int *rbl = (int *)(uil + Bp);          // rbl[i] + j = packed index of U_ij
+    int *rbl = (int *)(uil + Bp);          // rbl[i] + j = packed index of U_ij (for the MFMA lanes)
     float *El = (float *)(rbl + Bp);       // the chunk's errors [16 rows][ELD]
     const int tid = threadIdx.x;
     const int rl = tid >> 4, c = tid & 15;
@@ -153,90 +169,121 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
     const bool row_ok = row < a.d_out;
     const int64_t d_in = a.d_in, d_out = a.d_out;
 
-    // Stage the W tile, the packed upper part of the U block and 1/U_kk with
-    // 16-byte loads (4-column groups), all of a thread's loads issued before
-    // any is stored: U comes from HBM and one latency per block is the goal.
-    // Thread mapping without divisions: lane & 31 picks the 4-column group
-    // (plus 32 per half for blocks wider than 128 columns), tid >> 5 plus 8q
-    // the row.  full: every group of the block is 4 valid, 16-byte aligned
-    // columns, so no load needs a per-column bound.
+    // Stage the W tile, the packed upper part of the U block and 1/U_kk.
+    // Only the strict upper part of U is ever read (1/U_kk comes from uil);
+    // row i's packed range starts at column 4 floor(i/4), zeros on and below
+    // the diagonal.  full: every 4-column group of the block is 4 valid,
+    // 16-byte aligned columns.  Then all of a thread's 16-byte loads are
+    // issued before any is stored (U comes from HBM and one latency per block
+    // is the goal), each from an address clamped into range and zeroed
+    // afterwards, so that they carry no branches.  Thread mapping without
+    // divisions: lane & 31 picks the 4-column group (plus 32 per half for
+    // blocks wider than 128 columns), tid >> 5 plus 8q the row.  Otherwise
+    // (unaligned shapes) one element at a time on its own bounds.
     const bool full = (d_in % 4 == 0) && (b % 4 == 0) && (nb % 4 == 0);
-    auto load4 = [&](const float *p, int nvalid) -> f32x4 {
-        if (full) return *(const f32x4 *)p;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (nvalid > 0) v.x = p[0];
-        if (nvalid > 1) v.y = p[1];
-        if (nvalid > 2) v.z = p[2];
-        if (nvalid > 3) v.w = p[3];
-        return v;
-    };
     const int G = Bp / 4;                  // 4-column groups per row (<= 64)
     const int jg0 = tid & 31, ri = tid >> 5;
-    {
-        const int nhalf = (G + 31) / 32;   // 1 or 2
-        f32x4 wv[2][2], uv[2][16];
-        // W tile: 16 rows
+    auto store_u = [&](int i, int jg, f32x4 x) {
+        const int j = 4 * jg;
+        if (i < Bp && jg < G && j >= 4 * (i >> 2)) {
+            x.x = (j + 0 > i) ? x.x : 0.f;
+            x.y = (j + 1 > i) ? x.y : 0.f;
+            x.z = (j + 2 > i) ? x.z : 0.f;
+            x.w = (j + 3 > i) ? x.w : 0.f;
+            *(f32x4 *)(Ul + uidx(i, j, Bp)) = x;
+        }
+    };
+    auto stage_full = [&](auto nh_c) {
+        constexpr int NH = decltype(nh_c)::value;        // 32-group halves: 1 up to 128 columns, else 2
+        // rows and columns past the block (or past d_out) are read from a
+        // clamped, in-range address and zeroed when stored; 32-bit element
+        // offsets from a per-block base keep the address arithmetic short
+        const int di = (int)d_in, nbq = nb / 4;
+        const int rows_here = (int)std::min<int64_t>(QROWS, d_out - row0);
+        const float *wb = a.Wp + row0 * d_in + b;
+        const float *ub = a.U + (int64_t)b * d_in + b;
+        f32x4 wv[NH][2], uv[NH][16];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int jg = jg0 + 32 * hh, r = ri + 8 * q, j = 4 * jg;
-                const int64_t gr = row0 + r;
-                wv[hh][q] = (hh < nhalf && jg < G && gr < d_out && j < nb) ? load4(a.Wp + gr * d_in + b + j, nb - j)
-                                                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int jc = 4 * min(jg0 + 32 * hh, nbq - 1);
+                wv[hh][q] = *(const f32x4 *)(wb + (unsigned)(min(ri + 8 * q, rows_here - 1) * di + jc));
             }
         // U block rows 0..127 (rows 128..255 of a wider block in a second pass)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int jg = jg0 + 32 * hh, i = ri + 8 * q, j = 4 * jg;
-                uv[hh][q] = (hh < nhalf && jg < G && i < nb && j + 3 > i && j < nb)
-                                ? load4(a.U + (int64_t)(b + i) * d_in + b + j, nb - j)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int jc = 4 * min(jg0 + 32 * hh, nbq - 1);
+                uv[hh][q] = *(const f32x4 *)(ub + (unsigned)(min(ri + 8 * q, nb - 1) * di + jc));
             }
-        const float uiv = (tid < nb) ? a.uinv[b + tid] : 0.f;   // Bp <= 256: one per thread
+        const float uiv0 = a.uinv[b + min(tid, nb - 1)];   // Bp <= 256: one per thread
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int jg = jg0 + 32 * hh, r = ri + 8 * q;
-                if (hh < nhalf && jg < G) *(f32x4 *)(Wl + r * LW + 4 * jg) = wv[hh][q];
+                if (jg < G) *(f32x4 *)(Wl + r * LW + 4 * jg) = (r < rows_here && jg < nbq) ? wv[hh][q] : z;
             }
-        // only the strict upper part of U is ever read (1/U_kk comes from uil);
-        // row i's packed range starts at column 4 floor(i/4)
-        auto store_u = [&](int i, int jg, f32x4 x) {
-            const int j = 4 * jg;
-            if (i < Bp && jg < G && j >= 4 * (i >> 2)) {
-                x.x = (j + 0 > i) ? x.x : 0.f;
-                x.y = (j + 1 > i) ? x.y : 0.f;
-                x.z = (j + 2 > i) ? x.z : 0.f;
-                x.w = (j + 3 > i) ? x.w : 0.f;
-                *(f32x4 *)(Ul + uidx(i, j, Bp)) = x;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int jg = jg0 + 32 * hh, i = ri + 8 * q;
+                store_u(i, jg, (i < nb && jg < nbq) ? uv[hh][q] : z);
             }
-        };
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                if (hh < nhalf) store_u(ri + 8 * q, jg0 + 32 * hh, uv[hh][q]);
-        if (tid < Bp) {
-            uil[tid] = uiv;
-            rbl[tid] = uidx(tid, 0, Bp);
-        }
-        if (Bp > 128) {
+        if (tid < Bp) uil[tid] = (tid < nb) ? uiv0 : 0.f;
+        if (NH > 1) {
             // rows 128..Bp-1 (only their columns >= 128 are in the packed range)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int jg = jg0 + 32, i = 128 + ri + 8 * q, j = 4 * jg;
-                uv[0][q] = (jg < G && i < nb && j + 3 > i && j < nb)
-                               ? load4(a.U + (int64_t)(b + i) * d_in + b + j, nb - j)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int jc = 4 * min(jg0 + 32, nbq - 1);
+                uv[0][q] = *(const f32x4 *)(ub + (unsigned)(min(128 + ri + 8 * q, nb - 1) * di + jc));
             }
 #pragma unroll
-            for (int q = 0; q < 16; ++q) store_u(128 + ri + 8 * q, jg0 + 32, uv[0][q]);
+            for (int q = 0; q < 16; ++q) {
+                const int jg = jg0 + 32, i = 128 + ri + 8 * q;
+                store_u(i, jg, (i < nb && jg < nbq) ? uv[0][q] : z);
+            }
         }
+    };
+    if (full) {
+        if (G <= 32)
+            stage_full(std::integral_constant<int, 1>{});
+        else
+            stage_full(std::integral_constant<int, 2>{});
+    } else {
+        for (int it = tid; it < QROWS * G; it += 256) {
+            const int r = it / G, j = 4 * (it % G);
+            const int64_t gr = row0 + r;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (gr < d_out) {
+                const float *p = a.Wp + gr * d_in + b + j;
+                if (j + 0 < nb) v.x = p[0];
+                if (j + 1 < nb) v.y = p[1];
+                if (j + 2 < nb) v.z = p[2];
+                if (j + 3 < nb) v.w = p[3];
+            }
+            *(f32x4 *)(Wl + r * LW + j) = v;
+        }
+        for (int it = tid; it < Bp * G; it += 256) {
+            const int i = it / G, jg = it % G, j = 4 * jg;
+            if (j < 4 * (i >> 2)) continue;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (i < nb) {
+                const float *p = a.U + (int64_t)(b + i) * d_in + b + j;
+                if (j + 0 < nb && j + 0 > i) v.x = p[0];
+                if (j + 1 < nb && j + 1 > i) v.y = p[1];
+                if (j + 2 < nb && j + 2 > i) v.z = p[2];
+                if (j + 3 < nb && j + 3 > i) v.w = p[3];
+            }
+            store_u(i, jg, v);
+        }
+        if (tid < Bp) uil[tid] = (tid < nb) ? a.uinv[b + tid] : 0.f;
     }
+    if (tid < Bp) rbl[tid] = uidx(tid, 0, Bp);
     __syncthreads();
 
     if (a.near_k > 0) {
@@ -304,6 +351,10 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
                             maxq);
     }
 
+    const int cl = c;
+    // the first chunk's coefficients; later chunks' are read one chunk ahead
+    float u[CH], ui[CH];
+    load_coef(Ul, uil, 0, Bp, cl, u, ui);
     for (int c0 = 0; c0 < nb; c0 += CH) {
         const int k = b + c0;
         if (k % g == 0) {
@@ -336,52 +387,30 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
             }
         }
         float w = Wl[rl * LW + c0 + c];
-        float myq = 0.f, myE = 0.f;
-        // this chunk's coefficients in registers, off the dependency chain:
-        // u[S] = U_{c0+S, c0+c} for c > S (0 otherwise), ui[S] = 1/U_{c0+S, c0+S}
-        float u[CH], ui[CH];
-        // the lane's column, opaque to the optimizer: keeps the per-step lane
-        // masks from being hoisted out of the chunk loop (scalar spills)
-        int cl;
-        asm volatile("v_mov_b32 %0, %1" : "=v"(cl) : "v"(c));
-        {
-            // c0 is a multiple of 16 and Bp of 16: rows c0..c0+15 all exist in
-            // LDS (past nb they hold zeros); max(cl, S) stays inside row
-            // c0+S's packed range, which starts at column c0 + 4 floor(S/4)
-            int rb[CH];
-#pragma unroll
-            for (int q = 0; q < CH / 4; ++q) {
-                const f32x4 x = *(const f32x4 *)(uil + c0 + 4 * q);
-                ui[4 * q + 0] = x.x;
-                ui[4 * q + 1] = x.y;
-                ui[4 * q + 2] = x.z;
-                ui[4 * q + 3] = x.w;
-                const i32x4 y = *(const i32x4 *)(rbl + c0 + 4 * q);
-                rb[4 * q + 0] = y.x;
-                rb[4 * q + 1] = y.y;
-                rb[4 * q + 2] = y.z;
-                rb[4 * q + 3] = y.w;
-            }
-#pragma unroll
-            for (int S = 0; S < CH; ++S) {
-                const float x = Ul[rb[S] + c0 + max(cl, S)];
-                u[S] = (cl > S) ? x : 0.f;
-            }
-        }
-        // s / U_kk, U_kc / U_kk and s U_kc / U_kk (the group's parameters are
-        // fixed within a chunk)
-        float su[CH], uu[CH], sv[CH];
+        const float uic = uil[c0 + c];         // 1/U_kk of this lane's column
+        // U_kc / U_kk and s U_kc / U_kk for the chunk's steps (the group's
+        // parameters are fixed within a chunk)
+        float uu[CH], sv[CH];
 #pragma unroll
         for (int S = 0; S < CH; ++S) {
-            su[S] = Q.s * ui[S];
             uu[S] = u[S] * ui[S];
-            sv[S] = u[S] * su[S];
+            sv[S] = uu[S] * Q.s;
         }
-        StepCtx cx{c0, cl, nb};
+        // the next chunk's coefficients: their LDS reads go out after this
+        // chunk's own (LDS reads return in order) and are in flight during
+        // this chunk's steps.  Unconditional (the last chunk rereads its
+        // own), so that the waits before the steps count exactly.
+        __builtin_amdgcn_sched_barrier(0);
+        load_coef(Ul, uil, (c0 + CH < nb) ? c0 + CH : c0, Bp, cl, u, ui);
+        __builtin_amdgcn_sched_barrier(0);
         if (c0 + CH <= nb)
-            run_chunk<false>(w, myq, myE, cx, Q, uu, sv, ui, su, std::make_integer_sequence<int, CH>{});
+            run_chunk<false>(w, c0, nb, Q, uu, sv, std::make_integer_sequence<int, CH>{});
         else
-            run_chunk<true>(w, myq, myE, cx, Q, uu, sv, ui, su, std::make_integer_sequence<int, CH>{});
+            run_chunk<true>(w, c0, nb, Q, uu, sv, std::make_integer_sequence<int, CH>{});
+        // this lane's column: code and error, (w - s (q - z)) / U_kk
+        const float rq = __builtin_amdgcn_fmed3f(rintf(w * Q.inv_s), Q.lo, Q.hi);
+        const float myq = rq + Q.z;
+        const float myE = fmaf(-Q.s, rq, w) * uic;
         if (row_ok && c0 + c < nb) {
             a.codes[(int64_t)(k + c) * d_out + row] = (uint8_t)myq;
             a.E[(int64_t)(c0 + c) * d_out + row] = myE;
