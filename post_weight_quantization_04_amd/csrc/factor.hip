@@ -191,22 +191,29 @@ __device__ __forceinline__ void potrf_block_load(const float *__restrict__ src, 
     const int t = threadIdx.x, c4 = 4 * (t & 31);
     const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && (ld % 4 == 0) && (kb % 4 == 0);
     f32x4 v[16];
+    if (vec && kb == NB) {
+        // full block: every load unguarded (the upper triangle is read and
+        // dropped below), so that all sixteen are in flight together
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int i = (t >> 5) + 8 * q;
-        const float *p = src + (int64_t)i * ld + c4;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (i < kb && c4 <= i) {
-            if (vec) {
-                x = *(const f32x4 *)p;
-            } else {
-                if (c4 + 0 < kb) x.x = p[0];
-                if (c4 + 1 < kb) x.y = p[1];
-                if (c4 + 2 < kb) x.z = p[2];
-                if (c4 + 3 < kb) x.w = p[3];
+        for (int q = 0; q < 16; ++q) v[q] = *(const f32x4 *)(src + (int64_t)((t >> 5) + 8 * q) * ld + c4);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = (t >> 5) + 8 * q;
+            const float *p = src + (int64_t)i * ld + c4;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (i < kb && c4 <= i) {
+                if (vec) {
+                    x = *(const f32x4 *)p;
+                } else {
+                    if (c4 + 0 < kb) x.x = p[0];
+                    if (c4 + 1 < kb) x.y = p[1];
+                    if (c4 + 2 < kb) x.z = p[2];
+                    if (c4 + 3 < kb) x.w = p[3];
+                }
             }
+            v[q] = x;
         }
-        v[q] = x;
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -220,20 +227,23 @@ __device__ __forceinline__ void potrf_block_load(const float *__restrict__ src, 
     }
 }
 
-// dinv = the lower triangle of F restricted to kb x kb, zero elsewhere
+// dinv = the lower triangle of F restricted to kb x kb, zero elsewhere.
+// Thread t takes 4-column group t % 32 of rows t / 32 + 8q: 16-byte stores.
 __device__ __forceinline__ void potrf_block_store(const float *F, int kb, float *__restrict__ dinv) {
-    const int tid = threadIdx.x;
+    const int t = threadIdx.x, c4 = 4 * (t & 31);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        float v[32];
+    for (int q = 0; q < 16; ++q) {
+        const int i = (t >> 5) + 8 * q;
+        float e[4];
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int idx = tid + 256 * (32 * half + q);
-            const int i = idx >> 7, c = idx & (NB - 1);
-            v[q] = (i < kb && c < kb && c <= i) ? F[i * FLD + c] : 0.f;
+        for (int u = 0; u < 4; ++u) {
+            // kept iff c <= i < kb (then c < kb too), as an all-ones mask:
+            // plain integer arithmetic rather than 64 live lane masks
+            const int c = c4 + u;
+            const int keep = ((c - i - 1) & (i - kb)) >> 31;
+            e[u] = __builtin_bit_cast(float, __builtin_bit_cast(int, F[i * FLD + c]) & keep);
         }
-#pragma unroll
-        for (int q = 0; q < 32; ++q) dinv[tid + 256 * (32 * half + q)] = v[q];
+        *(f32x4 *)(dinv + i * NB + c4) = f32x4{e[0], e[1], e[2], e[3]};
     }
 }
 
@@ -525,89 +535,76 @@ __device__ __forceinline__ void signal_count(int32_t *cnt) {
 
 // Helper q of step k: quadrant (qa, qb) = (0,0), (1,0), (1,1) of the next
 // diagonal tile (k+1, k+1) of R takes C -= P_a P_b^T in place, with P the
-// panel rows of block k+1 (rows x kb, k-contiguous, at the panel's start).
-// The P rows of the two 64-row halves are staged in LDS ([row][k], stride
-// FLD); wave w takes the 32x32 sub-block (w/2, w%2) of the quadrant (none
-// above the diagonal of a diagonal quadrant) on fp32 MFMA, computed
-// transposed (lane (h, li), register 4a+b: row li, column 8a+4h+b).
-__device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, int n0, int rows, int kb, int q,
-                                              const float *__restrict__ P, float *lds) {
+// panel rows of block k+1 (rows x NB, k-contiguous, at the panel's start).
+// Wave w takes the 32x32 sub-block (w/2, w%2) of the quadrant (none above
+// the diagonal of a diagonal quadrant) on fp32 MFMA, computed transposed
+// (lane (h, li), register 4a+b: row li, column 8a+4h+b).  The products run
+// over k in any order as long as both operands agree, so lane half h
+// supplies k = 64h + s at step s: every lane reads its two P rows' 64 values
+// as 16-byte loads straight into registers, all issued together, and the
+// 64 products then run back to back.  Rows past the block read a clamped
+// row and only feed entries that are not stored.
+__device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, int n0, int rows, int q,
+                                              const float *__restrict__ P) {
     const int qa = (q >= 1) ? 1 : 0, qb = (q == 2) ? 1 : 0;
     const int ra = 64 * qa, rb = 64 * qb;
     if (ra >= rows) return;   // the block has no such quadrant
     const int tid = threadIdx.x;
-    // stage P rows [ra, ra+64) as operand 0 and [rb, rb+64) as operand 1
-    // (the same rows for a diagonal quadrant), zero past rows / kb
-    const int nop = (qa == qb) ? 1 : 2;
-    for (int op = 0; op < nop; ++op) {
-        const int r0 = op ? rb : ra;
-        f32x4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int f = tid + 256 * u;                 // 64 rows x 32 groups
-            const int r = f >> 5, k4 = 4 * (f & 31);
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (r0 + r < rows) {
-                const float *src = P + (int64_t)(r0 + r) * NB + k4;
-                if (k4 + 3 < kb) {
-                    x = *(const f32x4 *)src;
-                } else {
-                    if (k4 + 0 < kb) x.x = src[0];
-                    if (k4 + 1 < kb) x.y = src[1];
-                    if (k4 + 2 < kb) x.z = src[2];
-                }
-            }
-            v[u] = x;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int f = tid + 256 * u;
-            const int r = f >> 5, k4 = 4 * (f & 31);
-            float *dst = lds + (op * 64 + r) * FLD + k4;
-            dst[0] = v[u].x;
-            dst[1] = v[u].y;
-            dst[2] = v[u].z;
-            dst[3] = v[u].w;
-        }
-    }
-    __syncthreads();
     const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, li = lane & 31;
     const int sa = wave >> 1, sb = wave & 1;
     if (qa == qb && sa < sb) return;                       // above the diagonal: not needed
-    const int r = ra + 32 * sa + li;                       // this lane's row of the tile
+    const int r = ra + 32 * sa + li;                       // this lane's row of the tile (P_a row)
     const int cb = rb + 32 * sb;                           // the sub-block's first column
-    const float *Ar = lds + (32 * sa + li) * FLD;                        // P row ra + 32 sa + li
-    const float *Br = lds + ((nop - 1) * 64 + 32 * sb + li) * FLD;      // P row rb + 32 sb + li
     float *Crow = R + (int64_t)(n0 + r) * d + n0;
+    // acc = -C, then acc += P_b P_a^T (transposed), C = -acc.  A full tile
+    // (every step but the last) loads C without guards, before the operands,
+    // so that both sets of loads are in flight together.
+    f32x4 cv[4];
+    if (rows == NB) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) cv[a] = *(const f32x4 *)(Crow + cb + 8 * a + 4 * h);
+    } else {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int c = cb + 8 * a + 4 * h;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (r < rows) {
+                if (c + 3 < rows) {
+                    x = *(const f32x4 *)(Crow + c);
+                } else {
+                    if (c + 0 < rows) x.x = Crow[c + 0];
+                    if (c + 1 < rows) x.y = Crow[c + 1];
+                    if (c + 2 < rows) x.z = Crow[c + 2];
+                }
+            }
+            cv[a] = x;
+        }
+    }
+    const float *pa = P + (int64_t)min(r, rows - 1) * NB + 64 * h;
+    const float *pb = P + (int64_t)min(cb + li, rows - 1) * NB + 64 * h;
+    f32x4 av[16], bv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        av[j] = *(const f32x4 *)(pa + 4 * j);
+        bv[j] = *(const f32x4 *)(pb + 4 * j);
+    }
+    // every load goes out before the first product (one memory latency)
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 acc;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        const int c = cb + 8 * a + 4 * h;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (r < rows) {
-            if (c + 3 < rows) {
-                x = *(const f32x4 *)(Crow + c);
-            } else {
-                if (c + 0 < rows) x.x = Crow[c + 0];
-                if (c + 1 < rows) x.y = Crow[c + 1];
-                if (c + 2 < rows) x.z = Crow[c + 2];
-            }
-        }
-        acc[4 * a + 0] = x.x;
-        acc[4 * a + 1] = x.y;
-        acc[4 * a + 2] = x.z;
-        acc[4 * a + 3] = x.w;
+        acc[4 * a + 0] = -cv[a].x;
+        acc[4 * a + 1] = -cv[a].y;
+        acc[4 * a + 2] = -cv[a].z;
+        acc[4 * a + 3] = -cv[a].w;
     }
-#pragma unroll 8
-    for (int kk = 0; kk < NB; kk += 2) {
-        const int kx = kk + h;
-        // D[n][m] += sum_k B(k, n) A(k, m) with A = -P_a, B = P_b
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Br[kx], -Ar[kx], acc, 0, 0, 0);
-    }
+#pragma unroll
+    for (int s = 0; s < 64; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[s >> 2][s & 3], av[s >> 2][s & 3], acc, 0, 0, 0);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int c = cb + 8 * a + 4 * h;
-        const f32x4 x = {acc[4 * a + 0], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+        const f32x4 x = {-acc[4 * a + 0], -acc[4 * a + 1], -acc[4 * a + 2], -acc[4 * a + 3]};
         if (r < rows) {
             if (c + 3 < rows) {
                 *(f32x4 *)(Crow + c) = x;
@@ -639,7 +636,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
         const int n0 = (k + 1) * NB;
         const int rows = (int)std::min<int64_t>(NB, d - n0);
         if (b > 0) {
-            diag_quadrant(R, d, n0, rows, kb, b - 1, panel + (int64_t)(n0 - k1) * NB, lds);
+            diag_quadrant(R, d, n0, rows, b - 1, panel + (int64_t)(n0 - k1) * NB);
             signal_count(info + 1);
             return;
         }
