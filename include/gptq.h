@@ -49,7 +49,8 @@ typedef enum {
     GPTQ_OK = 0,
     GPTQ_EINVAL = 1,   /* bad argument (checked on the host, nothing launched) */
     GPTQ_ENOTSPD = 2,  /* damped Hessian not positive definite (a pivot <= 0 or NaN) */
-    GPTQ_EHIP = 3,     /* a HIP runtime call failed */
+    GPTQ_EHIP = 3,     /* a HIP runtime call failed, or a kernel's bounded wait for
+                          another work group gave up (reported, never hung on) */
     GPTQ_ENOMEM = 4    /* workspace smaller than the size query returned */
 } gptq_status;
 
@@ -116,7 +117,8 @@ GPTQ_API gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, 
  * Everything is enqueued on `stream`; the call then synchronizes `stream` once,
  * at the end, to read the factorization's positive-definiteness flag.
  * Errors: EINVAL, ENOMEM (nothing launched); ENOTSPD (outputs undefined);
- * EHIP.
+ * EHIP (also when the factorization's look-ahead gave up waiting for the
+ * groups updating its diagonal tile; outputs undefined).
  * ------------------------------------------------------------------------- */
 GPTQ_API size_t gptq_quantize_layer_workspace_size(int64_t d_out, int64_t d_in, int bits, int group_size,
                                           int block_size, int act_order);
