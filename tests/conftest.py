@@ -10,7 +10,7 @@ LIB = os.path.join(ROOT, "post_weight_quantization_04_amd", "libgptq.so")
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: long-running test, opt-in through GPTQ_FULL_PARITY=1")
+    config.addinivalue_line("markers", "slow: long-running test (tens of seconds, mostly host-side oracle work)")
 
 
 def pytest_sessionstart(session):

@@ -277,13 +277,10 @@ def test_identity_hessian_gives_rtn_on_gpu():
 
 
 # ---------------------------------------------------------------------------
-# full-size layers (opt-in: the oracle needs minutes of CPU per layer)
+# full-size layers in the benchmark's configuration (≈ 30-60 s each, most of
+# it the fp64 oracle Hessian on the host)
 # ---------------------------------------------------------------------------
-FULL = os.environ.get("GPTQ_FULL_PARITY") == "1"
-
-
 @pytest.mark.slow
-@pytest.mark.skipif(not FULL, reason="full-size layer parity is opt-in (GPTQ_FULL_PARITY=1): minutes of CPU oracle")
 @pytest.mark.parametrize("name,rows", [("q_proj", 96), ("up_proj", 96), ("down_proj", 64)])
 def test_full_layer_sampled_rows(name, rows):
     """Whole layer on the GPU in the benchmark's configuration; the oracle
