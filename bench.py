@@ -82,7 +82,7 @@ def cpu_baseline(wl, W, X):
     with threadpool_limits(limits=cores, user_api="blas"):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
         d_s = min(wl.d_in, 4096)
-        n_s = int(min(wl.n, max(512, 3e12 // (2 * d_s * d_s))))
+        n_s = int(min(wl.n, max(512, 1e13 // (2 * d_s * d_s))))
         r_s = min(wl.d_out, 512)
         t0 = time.perf_counter()
         H = O.hessian([X[:n_s, :d_s]], wl.dtype, d_s)
