@@ -21,7 +21,10 @@
 // with a coefficient preloaded into registers for the chunk.  After a chunk,
 // its 16 x 16 errors go to LDS and the rest of the block takes
 // W[16 rows, j] -= E[16 x 16] U[16, j] as 16 x 16 column tiles on fp32 MFMA
-// (v_mfma_f32_16x16x4_f32), the four waves taking every fourth tile.
+// (v_mfma_f32_16x16x4_f32), the four waves taking every fourth tile.  Before
+// the first chunk the pending blocks' errors are applied to the block's own
+// columns (the near update); for full 128-column blocks their U and E rows
+// stream through an LDS ring of 64-row chunks moved by 16-byte buffer loads.
 #include "common.h"
 
 #include <algorithm>
@@ -48,6 +51,123 @@ __host__ __device__ inline int uoff(int i, int Bp) {
 __host__ __device__ inline int usize(int Bp) { return uoff(Bp, Bp); }
 __device__ __forceinline__ int uidx(int i, int j, int Bp) { return uoff(i, Bp) + j - 4 * (i >> 2); }
 constexpr int ELD = CH + 1;   // row stride of the chunk's error tile in LDS
+
+// Near-update ring (full 128-column blocks with 16-byte aligned rows): 64
+// k-rows of U (128 columns) and of E (the group's 16 rows) per chunk, three
+// chunks in LDS, moved by 16-byte buffer loads straight into LDS.
+constexpr int NCH = 64;                        // k-rows per chunk
+constexpr int NUF = NCH * 128;                 // U chunk (floats), [k][128], 16-byte groups swizzled
+constexpr int NEF = NCH * QROWS;               // E chunk (floats), [k][16]
+constexpr int NSTG = 3;                        // ring stages
+constexpr int NRING = NSTG * (NUF + NEF);      // ring (floats)
+constexpr int NDMA = 9;                        // buffer loads per wave per chunk: 8 of U, 1 of E
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// work-group barrier without __syncthreads()' fence, which would also wait for
+// the chunks still meant to be in flight; this wave's LDS operations are
+// drained first, and chunk arrival is covered by the vmcnt waits
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// buffer resource over [p, p + bytes), base and size kept in scalar registers
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *p, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(p);
+    const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) << 32) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)b);
+    const int n = __builtin_amdgcn_readfirstlane((int)std::max<int64_t>(bytes, 0));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)bu, (short)0, n, 0x00020000);
+}
+
+// W[16 rows][0:128) -= E[16 rows][0:nk) U[0:nk)[0:128) for a full 128-column
+// block, the near update's fast path.  Wl: the staged W tile (row stride LW);
+// ring: NRING floats of LDS, 16-byte aligned.  U rows come from u (row
+// stride d_in), E rows from En (row stride d_out) at the group's row row0;
+// the buffer resources end at row nk, so the ragged last chunk reads zeros.
+// U chunk layout: k-row r holds column group g (4 columns) at slot
+// g ^ 4 (r % 4), so that the product's reads (16 columns of 4 k-rows per
+// instruction) hit 64 distinct banks.  Wave w takes column tiles 16w and
+// 16w + 64 on v_mfma_f32_16x16x4_f32 (A[i][k] at lane i + 16k, B[k][j] at
+// lane j + 16k, D[i][j] at lane 16 (i/4) + j, register i % 4), its
+// accumulators kept across all chunks.
+__device__ __forceinline__ void near_update_ring(float *Wl, int LW, float *ring, const float *u, const float *En,
+                                                 int64_t row0, int64_t d_in, int64_t d_out, int nk) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15, lk = lane >> 4;
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(u, ((int64_t)(nk - 1) * d_in + 128) * 4);
+    // E ends exactly at row nk (its rows past nk may hold anything, even
+    // NaN, which a zero U row would not cancel); rows of the group past d_out
+    // in its last k-row read zeros, and earlier ones only feed rows not stored
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(En + row0, ((int64_t)nk * d_out - row0) * 4);
+    // U: instruction q of wave w moves k-rows 16w + 2q (lanes 0-31) and +1
+    // (lanes 32-63), slot lane % 32 of each; E: one instruction per wave,
+    // k-rows 16w + lane / 4, 16-byte group lane % 4 of the 16 rows
+    int offu[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int r = 16 * wave + 2 * q + (lane >> 5);
+        const int g = (lane & 31) ^ (4 * (r & 3));
+        offu[q] = (int)((r * d_in + 4 * g) * 4);
+    }
+    const int offe = (int)(((16 * wave + (lane >> 2)) * d_out + 4 * (lane & 3)) * 4);
+    const int nch = (nk + NCH - 1) / NCH;
+    auto issue = [&](int c) {
+        lds_char *st = (lds_char *)(ring + (c % NSTG) * (NUF + NEF));
+        const int su = (int)(c * NCH * d_in * 4), se = (int)(c * NCH * d_out * 4);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void_t *)(st + (16 * wave + 2 * q) * 128 * 4), 16,
+                                                     offu[q] + su, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void_t *)(st + (NUF + 16 * wave * QROWS) * 4), 16, offe + se,
+                                                 0, 0, 0);
+    };
+    issue(0);
+    if (nch > 1) issue(1);
+    const int jp = 16 * wave, j1 = jp + 64;
+    f32x4 acc0, acc1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        acc0[r] = Wl[(4 * lk + r) * LW + jp + li];
+        acc1[r] = Wl[(4 * lk + r) * LW + j1 + li];
+    }
+    // this lane's U columns jp + li and j1 + li, swizzled by its k-row's r % 4 = lk
+    const int cu0 = 4 * (((jp + li) >> 2) ^ (4 * lk)) + (li & 3);
+    const int cu1 = 4 * (((j1 + li) >> 2) ^ (4 * lk)) + (li & 3);
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch)
+            wait_vm<NDMA>();   // chunk c landed, chunk c + 1 may be in flight
+        else
+            wait_vm<0>();
+        lds_barrier();         // every wave's part of chunk c, and every wave done with chunk c - 1
+        if (c + 2 < nch) issue(c + 2);
+        const float *st = ring + (c % NSTG) * (NUF + NEF);
+        float ea[16], ub0[16], ub1[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int k = 4 * t + lk;
+            ea[t] = -st[NUF + k * QROWS + li];
+            ub0[t] = st[k * 128 + cu0];
+            ub1[t] = st[k * 128 + cu1];
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub0[t], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub1[t], acc1, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        Wl[(4 * lk + r) * LW + jp + li] = acc0[r];
+        Wl[(4 * lk + r) * LW + j1 + li] = acc1[r];
+    }
+}
 
 // lane S of each 16-lane DPP row to the whole row (every lane is written, so
 // no old value is needed)
@@ -286,7 +406,14 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
     if (tid < Bp) rbl[tid] = uidx(tid, 0, Bp);
     __syncthreads();
 
-    if (a.near_k > 0) {
+    const bool near_fast = nb == 128 && d_in % 4 == 0 && d_out % 4 == 0 && b % 4 == 0 &&
+                           a.near_k * std::max(d_in, d_out) * 4 + (int64_t)NSTG * NCH * std::max(d_in, d_out) * 4 <
+                               ((int64_t)1 << 31);
+    if (a.near_k > 0 && near_fast) {
+        float *ring = El + ((QROWS * ELD + 3) & ~3);   // 16-byte aligned after the error tile
+        near_update_ring(Wl, LW, ring, a.U + a.near_row0 * d_in + b, a.En, row0, d_in, d_out, a.near_k);
+        __syncthreads();
+    } else if (a.near_k > 0) {
         // The pending blocks' errors on this block's columns:
         //   W[16 rows][j] -= sum_{k < near_k} En[k][row] U[near_row0 + k][b + j]
         // as 16 x 16 tiles on v_mfma_f32_16x16x4_f32 (A[i][k] at lane i + 16k,
@@ -477,7 +604,9 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b0, i
 
 size_t quant_lds_bytes(int block) {
     const int Bp = roundup16(block);
-    return sizeof(float) * ((size_t)QROWS * (Bp + 4) + (size_t)usize(Bp) + 2 * (size_t)Bp + (size_t)QROWS * ELD);
+    const size_t base = (size_t)QROWS * (Bp + 4) + (size_t)usize(Bp) + 2 * (size_t)Bp + (size_t)((QROWS * ELD + 3) & ~3);
+    // blocks of 128 columns take the near update through the LDS ring
+    return sizeof(float) * (base + (block == 128 ? (size_t)NRING : 0));
 }
 
 int quant_cu_count() {
