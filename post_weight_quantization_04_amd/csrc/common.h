@@ -97,7 +97,7 @@ hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64
 // lazy update): each block's in-block kernel first takes the pending blocks'
 // errors on its own columns, and every FAR_BLOCKS blocks one product applies
 // all pending errors to the columns beyond.
-constexpr int FAR_BLOCKS = 4;
+constexpr int FAR_BLOCKS = 8;
 // W[:, c_begin:c_end) -= E[0:K) (as [K][d_out]) U[u_row0 : u_row0+K, c_begin:c_end)
 hipError_t trail_launch(const QuantArgs &a, int64_t u_row0, int64_t K, int64_t c_begin, int64_t c_end,
                         hipStream_t st);
