@@ -49,9 +49,15 @@ def describe(wl):
 
 
 def kernel_source_hash():
+    """sha256 of the Hessian kernels' source: hessian.hip and the part of
+    common.h they use (the shared types and the Hessian declarations, up to
+    the next section)."""
+    csrc = os.path.join(ROOT, "post_weight_quantization_04_amd", "csrc")
+    common = open(os.path.join(csrc, "common.h"), "rb").read()
+    cut = common.find(b"// Preparation (prep.hip)")
     h = hashlib.sha256()
-    for f in ("hessian.hip", "common.h"):
-        h.update(open(os.path.join(ROOT, "post_weight_quantization_04_amd", "csrc", f), "rb").read())
+    h.update(open(os.path.join(csrc, "hessian.hip"), "rb").read())
+    h.update(common[:cut] if cut >= 0 else common)
     return h.hexdigest()
 
 
