@@ -149,7 +149,7 @@ Workspace layout(const LayerShape &L, char *base) {
     const int64_t d = L.d_in;
     w.R = (float *)take(sizeof(float) * (size_t)d * d);
     w.Wp = (float *)take(sizeof(float) * (size_t)L.d_out * d);
-    w.E = (float *)take(sizeof(float) * (size_t)gptq::FAR_BLOCKS * L.block_int * L.d_out);
+    w.E = (float *)take(sizeof(float) * (size_t)gptq::far_blocks(L.block_int) * L.block_int * L.d_out);
     w.codes = (uint8_t *)take((size_t)d * L.d_out);
     w.panel = (float *)take(sizeof(float) * (size_t)d * gptq::FACT_NB);
     w.dinv = (float *)take(sizeof(float) * 2 * gptq::FACT_NB * gptq::FACT_NB);  // ping-pong pair
@@ -347,7 +347,7 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
     qa.bits = bits;
     qa.group = L.group;
     qa.block = L.block_int;
-    // Blocks go in batches of FAR_BLOCKS; the errors of a batch's blocks are
+    // Blocks go in batches of far_blocks(B); the errors of a batch's blocks are
     // stacked in E (block t of the batch at rows t*B..).  One in-block launch
     // takes the whole batch, each block first applying the batch's earlier
     // errors to its own columns (the near update); then one product applies
@@ -356,11 +356,11 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
     // before such a group begins.
     const int64_t B = L.block_int;
     for (int64_t pend0 = 0; pend0 < d_in;) {
-        // one batch: up to FAR_BLOCKS blocks, ending early after a block whose
+        // one batch: up to far_blocks(B) blocks, ending early after a block whose
         // end starts a group wider than a block
         int nblk = 0;
         int64_t e = pend0;
-        while (nblk < gptq::FAR_BLOCKS && e < d_in) {
+        while (nblk < gptq::far_blocks(B) && e < d_in) {
             e = std::min<int64_t>(e + B, d_in);
             ++nblk;
             if (L.group > B && e % L.group == 0) break;

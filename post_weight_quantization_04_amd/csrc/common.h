@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <algorithm>
 
 namespace gptq {
 
@@ -95,9 +96,13 @@ size_t quant_lds_bytes(int block);
 hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64_t B, hipStream_t st);
 // Blocks whose errors are applied to the far columns together (two-level
 // lazy update): each block's in-block kernel first takes the pending blocks'
-// errors on its own columns, and every FAR_BLOCKS blocks one product applies
-// all pending errors to the columns beyond.
+// errors on its own columns, and after far_blocks(B) blocks one product
+// applies all pending errors to the columns beyond.  Blocks up to 128 columns
+// wide go eight at a time; wider ones (whose near update has no LDS left for a
+// staging ring) as many as fill 1024 columns.
 constexpr int FAR_BLOCKS = 8;
+constexpr int FAR_COLS_WIDE = 1024;
+inline int far_blocks(int64_t B) { return B <= 128 ? FAR_BLOCKS : (int)std::max<int64_t>(1, FAR_COLS_WIDE / B); }
 // W[:, c_begin:c_end) -= E[0:K) (as [K][d_out]) U[u_row0 : u_row0+K, c_begin:c_end)
 hipError_t trail_launch(const QuantArgs &a, int64_t u_row0, int64_t K, int64_t c_begin, int64_t c_end,
                         hipStream_t st);
