@@ -132,7 +132,7 @@ gptq_status check_layer(int64_t d_out, int64_t d_in, int bits, int group_size, i
 }
 
 struct Workspace {
-    float *R, *Wp, *E, *panel, *dinv, *dg, *ud, *uinv, *lam;
+    float *R, *Wp, *E, *panel, *pt, *dinv, *dg, *ud, *uinv, *lam;
     uint8_t *codes;
     int32_t *rank, *info;
     size_t bytes;
@@ -152,6 +152,7 @@ Workspace layout(const LayerShape &L, char *base) {
     w.E = (float *)take(sizeof(float) * (size_t)gptq::far_blocks(L.block_int) * L.block_int * L.d_out);
     w.codes = (uint8_t *)take((size_t)d * L.d_out);
     w.panel = (float *)take(sizeof(float) * (size_t)d * gptq::FACT_NB);
+    w.pt = (float *)take(gptq::factor_batch(d) > 1 ? sizeof(float) * (size_t)gptq::FACT_BATCH * gptq::FACT_NB * d : 0);
     w.dinv = (float *)take(sizeof(float) * 2 * gptq::FACT_NB * gptq::FACT_NB);  // ping-pong pair
     w.dg = (float *)take(sizeof(float) * d);
     w.ud = (float *)take(sizeof(float) * d);
@@ -175,7 +176,7 @@ gptq_status run_factor(const float *H, int64_t d, float damp, int act_order, int
     }
     {
         StageTimer t(3, st);
-        HIPCHECK(gptq::factor_launch(w.R, d, w.panel, w.dinv, w.info, st));
+        HIPCHECK(gptq::factor_launch(w.R, d, w.panel, w.pt, w.dinv, w.info, st));
     }
     return GPTQ_OK;
 }

@@ -65,7 +65,17 @@ constexpr int FACT_NB = 128;
 // FACTOR_SYNC_TIMEOUT if the look-ahead's wait for its helpers gave up;
 // info[1] counts the helpers' completed diagonal-tile updates.
 constexpr int32_t FACTOR_SYNC_TIMEOUT = -1;
-hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t *info,
+// Large matrices take the steps in batches of FACT_BATCH (two-level update):
+// inside a batch each step updates only the batch's own later columns and
+// rows, and one far update with K = 128 FACT_BATCH then applies the whole
+// batch to the rows below it.  factor_batch(d): the batch length used for
+// d (1: every step updates the whole trailing matrix).
+constexpr int FACT_BATCH = 8;
+constexpr int FACT_BATCH_MIN_BLOCKS = 64;
+int factor_batch(int64_t d);
+// pt: FACT_BATCH * FACT_NB * d floats when factor_batch(d) > 1 (the batch's
+// panels transposed), else unused.
+hipError_t factor_launch(float *R, int64_t d, float *panel, float *pt, float *dinv, int32_t *info,
                          hipStream_t st);
 // U[k][j] = M[d-1-k][d-1-j] for k < j (in place, upper triangle);
 // ud[k] = M[d-1-k][d-1-k]; uinv[k] = 1/ud[k].  zero_lower: clear the strictly

@@ -28,7 +28,19 @@
 // Dinv alternates between two buffers by step parity because the fused
 // potrf writes the next step's while the rest of the kernel reads this one.
 // The tile products run on fp32 MFMA (v_mfma_f32_32x32x2_f32).
+//
+// Batched schedule (factor_batch(d) = T > 1, large d): every step above
+// rewrites the whole trailing matrix with a K = 128 product, so for large d
+// the factorization streams the matrix through HBM once per step.  Instead
+// the steps go in batches [s, e) of T.  Inside a batch, step k's update
+// kernel touches only what the batch's later panels read: the rows k+1..e-1
+// left of column k+1 (their S) and the columns k+1..e-1 from the diagonal
+// down (their A), with the look-ahead as before.  After the batch's last
+// panel one far update (far_kernel, K = 128 T) applies all T steps to the
+// rows below the batch, and potrf_kernel factors block e.  The panels also
+// go to pt transposed for it.  Same sums, fewer passes over the matrix.
 #include "common.h"
+#include "dma_tile.h"
 #include "tile_gemm.h"
 
 #include <algorithm>
@@ -456,8 +468,11 @@ __device__ __forceinline__ void store_strip(const f32x16 &acc, float *C, int64_t
 // part B (column blocks left of k, 32-column strips): M_kj = -Dinv S_kj, in
 //        place (each group reads and writes only its own columns of S)
 // last group: M_kk = Dinv
+// pt (batched schedule only, else null): part A also writes P transposed,
+// pt[pt_k + c][row] = P[row][c], for the batch's far update.
 __global__ __launch_bounds__(256) void panel_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
-                                                    float *__restrict__ panel, const float *__restrict__ dinv) {
+                                                    float *__restrict__ panel, const float *__restrict__ dinv,
+                                                    float *__restrict__ pt, int pt_k) {
     __shared__ __attribute__((aligned(16))) float lds[2 * GK * (GLD + SLD)];
     const int k0 = k * NB, kb = (int)std::min<int64_t>(NB, d - k0), k1 = k0 + kb;
     const int na = nblk - k - 1;
@@ -471,6 +486,20 @@ __global__ __launch_bounds__(256) void panel_kernel(float *__restrict__ R, int64
         // B(k, n) = Dinv[n][k]: k-contiguous rows of Dinv
         gemm_strip<true, true, true>(acc, A, d, dinv, NB, rows, kb, kb, 1.f, aligned16(A, d), lds);
         store_strip<true>(acc, panel + (int64_t)(row0 - k1) * NB, NB, rows, kb);
+        if (pt) {
+            // lane (h, li) holds row li, columns 32 w + 8a + 4h + b: each
+            // store puts 32 consecutive rows of one transposed row
+            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, li = lane & 31;
+            if (li < rows) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int c = wave * 32 + 8 * a + 4 * h + b;
+                        if (c < kb) pt[(int64_t)(pt_k + c) * d + row0 + li] = acc[4 * a + b];
+                    }
+            }
+        }
     } else if (bid < 4 * na + 4 * k) {
         const int col0 = ((bid - 4 * na) / 4) * NB + 32 * ((bid - 4 * na) % 4);
         float *S = R + (int64_t)k0 * d + col0;                   // S(k, n) = R[k0+k][col0+n]
@@ -622,12 +651,19 @@ __device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, 
 //                 tile (k+1, k+1) from R and factors it (look-ahead), writing
 //                 Dinv_{k+1} to dinv_next.
 //   groups 1..3 : the next diagonal tile's update, one 64x64 quadrant each.
-//   groups 4..  : every other tile in rows > k, as for the tile product:
-//                 (k+1, 0..k) first, then the rows below in order.
-__global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, int64_t d, int k, int nblk,
+//   groups 4..  : every other tile that step k updates now.  Unbatched
+//                 (e == nblk): all tiles in rows > k, (k+1, 0..k) first,
+//                 then the rows below in order.  Inside a batch of steps
+//                 ending at block e < nblk: the rows k+1 .. e-1 left of
+//                 column k+1 (row by row), then the columns k+1 .. e-1 from
+//                 their diagonal down (column by column); the rest of the
+//                 step's update waits for the batch's far update.
+// target: the helpers' count that group 0 waits for (three per launch).
+__global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, int64_t d, int k, int nblk, int e,
                                                      const float *__restrict__ panel,
                                                      const float *__restrict__ dinv_k,
-                                                     float *__restrict__ dinv_next, int32_t *__restrict__ info) {
+                                                     float *__restrict__ dinv_next, int32_t *__restrict__ info,
+                                                     int target) {
     __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
     __shared__ __attribute__((aligned(16))) float bc[64];
     const int k0 = k * NB, kb = (int)std::min<int64_t>(NB, d - k0), k1 = k0 + kb;
@@ -640,7 +676,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
             signal_count(info + 1);
             return;
         }
-        wait_count(info + 1, 3 * (k + 1), info);
+        wait_count(info + 1, target, info);
         float *F = lds;
         potrf_block_load(R + (int64_t)n0 * d + n0, d, rows, F);
         __syncthreads();
@@ -648,14 +684,35 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
         potrf_block_store(F, rows, dinv_next);
         return;
     }
-    // the tile product: (k+1, 0..k), then the rows below in order
-    const int bb = b - 3;
     int i, j;
-    if (bb <= k + 1) {
-        i = k + 1;
-        j = bb - 1;
+    if (e >= nblk) {
+        // (k+1, 0..k), then the rows below in order
+        const int bb = b - 3;
+        if (bb <= k + 1) {
+            i = k + 1;
+            j = bb - 1;
+        } else {
+            tile_coords((k + 1) * (k + 2) / 2 + bb, i, j);
+        }
     } else {
-        tile_coords((k + 1) * (k + 2) / 2 + bb, i, j);
+        int t = b - 4;
+        const int nrow = (e - k - 1) * (k + 1);
+        if (t < nrow) {
+            i = k + 1 + t / (k + 1);
+            j = t % (k + 1);
+        } else {
+            // column c holds rows c .. nblk-1, without (k+1, k+1)
+            t -= nrow;
+            int c = k + 1, n = nblk - k - 2;
+            while (t >= n && c < e) {
+                t -= n;
+                ++c;
+                n = nblk - c;
+            }
+            if (c >= e) return;   // past the last tile (the grid is sized exactly)
+            j = c;
+            i = (c == k + 1) ? c + 1 + t : c + t;
+        }
     }
     const int row0 = i * NB, col0 = j * NB;
     const int rows = (int)std::min<int64_t>(NB, d - row0);
@@ -679,6 +736,45 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
     store_c(acc, C, d, rows, cols);
 }
 
+// Far update of the batch of steps s .. e-1 (e < nblk), one 128 x 128 tile
+// (i, j) of the rows below the batch per work group, i >= e, j <= i, in row
+// order.  pt holds the batch's panels transposed ([(m - s) * 128 + c][row]
+// = L[row][128 m + c]), so with K = 128 (e - s):
+//   j >= e      : A_ij -= sum_m P_i^(m) P_j^(m)^T        (Cholesky part)
+//   s <= j < e  : S_ij  = sum_{m >= j} P_i^(m) M_mj      (M_jj = Dinv_j)
+//   j <  s      : S_ij += sum_m P_i^(m) M_mj
+// with the batch's rows of M read from R (final after its panels; the
+// diagonal blocks carry zeros above the diagonal).  The sums over the batch
+// equal the steps' own updates applied one after another, so the result is
+// the same factorization up to rounding order.
+__global__ __launch_bounds__(256, 1) void far_kernel(float *__restrict__ R, int64_t d, int s, int e,
+                                                  const float *__restrict__ pt) {
+    __shared__ __attribute__((aligned(16))) float lds[DmaShape<128>::LDS_FLOATS];
+    int i, j;
+    tile_coords(e * (e + 1) / 2 + (int)blockIdx.x, i, j);
+    const int64_t row0 = (int64_t)i * NB, col0 = (int64_t)j * NB;
+    const int rows = (int)std::min<int64_t>(NB, d - row0);
+    const int cols = (int)std::min<int64_t>(NB, d - col0);
+    if (rows <= 0) return;
+    const int kt = (e - s) * NB;   // every block of a batch that has a far update is full
+    int koff = 0, mode = DMA_ADD;
+    const float *B;
+    if (j >= e) {
+        mode = DMA_SUB;
+        B = pt + col0;
+    } else {
+        if (j >= s) {
+            koff = (j - s) * NB;
+            mode = DMA_SET;
+        }
+        B = R + (int64_t)(s * NB + koff) * d + col0;
+    }
+    const int K = kt - koff;
+    const float *A = pt + (int64_t)koff * d + row0;
+    dma_tile_product<128>(R + row0 * d + col0, d, rows, cols, A, d, ((int64_t)K * d - row0) * 4, B + 0, d,
+                          ((int64_t)K * d - col0) * 4, K, mode, lds);
+}
+
 __global__ void flip_kernel(float *__restrict__ R, int64_t d, float *__restrict__ ud) {
     // one row r per block: U[r][c] = M[d-1-r][d-1-c] for c > r, ud[r] = M[d-1-r][d-1-r]
     const int64_t r = blockIdx.x;
@@ -700,20 +796,55 @@ __global__ void finish_diag_kernel(float *__restrict__ R, int64_t d, const float
 
 }  // namespace
 
-hipError_t factor_launch(float *R, int64_t d, float *panel, float *dinv, int32_t *info, hipStream_t st) {
+int factor_batch(int64_t d) {
+    const int64_t nblk = cdiv(d, NB);
+    // the far update moves 16-byte rows with 32-bit offsets
+    if (d % 4 != 0 || (int64_t)FACT_BATCH * NB * d * 4 + (int64_t)DK * DNST * d * 4 >= ((int64_t)1 << 31)) return 1;
+    return nblk >= FACT_BATCH_MIN_BLOCKS ? FACT_BATCH : 1;
+}
+
+hipError_t factor_launch(float *R, int64_t d, float *panel, float *pt, float *dinv, int32_t *info, hipStream_t st) {
     const int nblk = (int)cdiv(d, NB);
+    const int T = factor_batch(d);
     float *dbuf[2] = {dinv, dinv + NB * NB};
     potrf_kernel<<<1, 256, 0, st>>>(R, d, 0, (int)std::min<int64_t>(NB, d), dbuf[0], info);
-    for (int k = 0; k < nblk; ++k) {
-        const int na = nblk - k - 1;
-        panel_kernel<<<4 * (na + k) + 1, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1]);
-        // tiles in rows > k besides the next diagonal one, plus the look-ahead
-        // group and its three helpers
-        const int nup = nblk * (nblk + 1) / 2 - (k + 1) * (k + 2) / 2;
-        if (nup > 0)
-            update_kernel<<<nup + 3, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1], dbuf[(k + 1) & 1], info);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    int target = 0;   // helpers' completions so far
+    for (int s = 0, e = 0; s < nblk; s = e) {
+        // batch [s, e); unbatched, one batch of all steps and no far update
+        e = (T > 1) ? std::min(nblk, s + T) : nblk;
+        const bool far = e < nblk;
+        for (int k = s; k < e; ++k) {
+            const int na = nblk - k - 1;
+            panel_kernel<<<4 * (na + k) + 1, 256, 0, st>>>(R, d, k, nblk, panel, dbuf[k & 1], far ? pt : nullptr,
+                                                           (k - s) * NB);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            if (far && k == e - 1) break;   // the far update takes the rest of this step
+            // tiles updated now, the next diagonal one included: that one goes
+            // to the three helpers, and group 0 is the look-ahead
+            int nup;
+            if (!far) {
+                nup = nblk * (nblk + 1) / 2 - (k + 1) * (k + 2) / 2;
+            } else {
+                nup = (e - k - 1) * (k + 1);
+                for (int c = k + 1; c < e; ++c) nup += nblk - c;
+            }
+            if (nup > 0) {
+                target += 3;
+                update_kernel<<<nup + 3, 256, 0, st>>>(R, d, k, nblk, e, panel, dbuf[k & 1], dbuf[(k + 1) & 1], info,
+                                                       target);
+                err = hipGetLastError();
+                if (err != hipSuccess) return err;
+            }
+        }
+        if (far) {
+            const int ntile = nblk * (nblk + 1) / 2 - e * (e + 1) / 2;
+            far_kernel<<<ntile, 256, 0, st>>>(R, d, s, e, pt);
+            potrf_kernel<<<1, 256, 0, st>>>(R, d, e * NB, (int)std::min<int64_t>(NB, d - (int64_t)e * NB), dbuf[e & 1],
+                                            info);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
     }
     return hipSuccess;
 }

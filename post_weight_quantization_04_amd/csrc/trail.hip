@@ -15,7 +15,8 @@
 // tile runs at the matrix cores' rate even when it has its unit to itself
 // (a launch's last, partial round).  The buffer resources end at row K of E
 // and U, so the ragged last chunk reads zeros without a branch; rows and
-// columns past the tile's edge only feed entries that are not stored.
+// columns past the tile's edge only feed entries that are not stored.  The
+// tile body (dma_tile.h) is shared with the factorization's far update.
 //
 // Fallback (trail_kernel, any shape): one work group per 128 x 128 tile of W, fp32 operands on fp32 MFMA
 // (v_mfma_f32_32x32x2_f32).  Both operands arrive as k-rows (E is [k][row],
@@ -26,6 +27,7 @@
 // loads go out after the first chunk's and the product starts from zero, so
 // the W tile's latency passes during the product; it is added at the end.
 #include "common.h"
+#include "dma_tile.h"
 
 #include <algorithm>
 
@@ -197,200 +199,25 @@ __global__ __launch_bounds__(256, 2) void trail_kernel(QuantArgs a, int u_row0, 
             }
 }
 
-constexpr int NST = 4;   // LDS ring stages of the main kernel
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) char lds_char;
-
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-
-// Work-group barrier without __syncthreads()' fence, which would also wait
-// for the chunks still meant to be in flight; this wave's LDS operations are
-// drained first, and chunk arrival is covered by the vmcnt waits.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// buffer resource over [p, p + bytes), base and size kept in scalar registers
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *p, int64_t bytes) {
-    const uint64_t b = reinterpret_cast<uint64_t>(p);
-    const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) << 32) |
-                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((unsigned)b);
-    const int n = __builtin_amdgcn_readfirstlane((int)std::max<int64_t>(bytes, 0));
-    return __builtin_amdgcn_make_buffer_rsrc((void *)bu, (short)0, n, 0x00020000);
-}
-
-// Requires d_out % 4 == 0, d_in % 4 == 0, c_begin % 4 == 0 (16-byte aligned
-// rows and tile origins) and K * max(d_out, d_in) * 4 < 2^31.  Tiles are
+// Main kernel: tile t is row tile t % tiles_m of column tile t / tiles_m,
 // 128 rows x TN columns (TN = 128, or 64 for the last columns of a launch
-// whose 128-wide tiles would leave a half-empty last round); tile t is row
-// tile t % tiles_m of column tile t / tiles_m.  Waves form a 2 x 2 grid of
-// 64 x TN/2 blocks (MB = TN/64 MFMA blocks across).
+// whose 128-wide tiles would leave a half-empty last round).  Requires
+// d_out % 4 == 0, d_in % 4 == 0, c_begin % 4 == 0 (16-byte aligned rows and
+// tile origins) and K * max(d_out, d_in) * 4 < 2^31.
+// A(k, m) = E[k][row0 + m] and B(k, n) = U[u_row0 + k][col0 + n] for k < K:
+// the buffer resources end at row K of E and U.
 template <int TN>
-struct DmaShape {
-    static constexpr int MB = TN / 64;                 // 32-column MFMA blocks per wave
-    static constexpr int BST = TK * TN;                // B chunk (floats)
-    static constexpr int STAGE = TSTAGE + BST;         // one ring stage: A chunk then B chunk
-    static constexpr int BROWS = 1024 / (TN * 4);      // B k-rows per 1 KB load instruction (2 or 4)
-    static constexpr int BINS = 8 / BROWS;             // B load instructions per wave per stage
-    static constexpr int PER_STAGE = 4 + BINS;         // vector-memory instructions per stage per wave
-};
-
-// one tile; lds: NST * DmaShape<TN>::STAGE floats.  (The body lives in a
-// device function: the host pass instantiates a kernel template's body, and
-// the buffer-resource type exists only for the device.)
-template <int TN>
-__device__ __forceinline__ void trail_dma_tile(const QuantArgs &a, int u_row0, int K, int c_begin, int c_end, int tiles_m,
-                                               float *lds) {
-    constexpr int MB = DmaShape<TN>::MB;
-    constexpr int STAGE = DmaShape<TN>::STAGE;
-    constexpr int BROWS = DmaShape<TN>::BROWS;
-    constexpr int BINS = DmaShape<TN>::BINS;
-    constexpr int PER_STAGE = DmaShape<TN>::PER_STAGE;
+__global__ __launch_bounds__(256, 1) void trail_dma_kernel(QuantArgs a, int u_row0, int K, int c_begin, int c_end,
+                                                        int tiles_m) {
+    __shared__ __attribute__((aligned(16))) float lds[DmaShape<TN>::LDS_FLOATS];
     const int t = blockIdx.x;
     const int64_t row0 = (int64_t)(t % tiles_m) * TT;
     const int64_t col0 = (int64_t)c_begin + (int64_t)(t / tiles_m) * TN;
     const int rows = (int)std::min<int64_t>(TT, a.d_out - row0);
     const int cols = (int)std::min<int64_t>(TN, c_end - col0);
-    const int64_t d_out = a.d_out, d_in = a.d_in;
-    float *C = a.Wp + row0 * d_in + col0;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
-    const int nch = (K + TK - 1) / TK;
-    // accumulator (ma, mb), register group g: W row wr*64 + ma*32 + li,
-    // columns wc*TN/2 + mb*32 + 8g + 4h + [0, 4)
-
-    // the W tile first: its loads are the oldest, covered by the first wait
-    f32x4 cv[2][MB][4];
-    const bool full_tile = rows == TT && cols == TN;
-#pragma unroll
-    for (int ma = 0; ma < 2; ++ma)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r = wr * 64 + ma * 32 + li, c = wc * (TN / 2) + mb * 32 + 8 * g + 4 * h;
-                const float *src = C + (int64_t)r * d_in + c;
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-                if (full_tile) {
-                    x = *(const f32x4 *)src;
-                } else if (r < rows) {
-                    if (c + 3 < cols) {
-                        x = *(const f32x4 *)src;
-                    } else {
-                        if (c + 0 < cols) x.x = src[0];
-                        if (c + 1 < cols) x.y = src[1];
-                        if (c + 2 < cols) x.z = src[2];
-                    }
-                }
-                cv[ma][mb][g] = x;
-            }
-
-    // A(k, m) = E[k][row0 + m] for k < K; B(k, n) = U[u_row0 + k][col0 + n]
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.E + row0, ((int64_t)K * d_out - row0) * 4);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.U + (int64_t)u_row0 * d_in + col0, ((int64_t)K * d_in - col0) * 4);
-    // wave w moves k-rows 8w .. 8w+7 of each chunk: A two rows per
-    // instruction (32 lanes x 16 bytes each), B BROWS rows per instruction
-    int offa[4], offb[BINS];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) offa[q] = (int)(((8 * wave + 2 * q + h) * d_out + 4 * li) * 4);
-    {
-        const int lpr = TN / 4;   // lanes per B row
-#pragma unroll
-        for (int q = 0; q < BINS; ++q)
-            offb[q] = (int)(((8 * wave + BROWS * q + lane / lpr) * d_in + 4 * (lane % lpr)) * 4);
-    }
-    auto issue = [&](int st) {
-        lds_char *buf = (lds_char *)lds + (st % NST) * STAGE * 4;
-        const int sa = (int)(st * TK * d_out * 4), sb = (int)(st * TK * d_in * 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(buf + (8 * wave + 2 * q) * TLD * 4), 16,
-                                                     offa[q] + sa, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < BINS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(buf + (TSTAGE + (8 * wave + BROWS * q) * TN) * 4),
-                                                     16, offb[q] + sb, 0, 0, 0);
-    };
-    for (int st = 0; st < NST - 1 && st < nch; ++st) issue(st);
-
-    f32x16_t acc[2][MB];
-#pragma unroll
-    for (int ma = 0; ma < 2; ++ma)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[ma][mb] = f32x16_t{};
-    for (int ch = 0; ch < nch; ++ch) {
-        // chunk ch landed: the chunks issued after it may stay in flight
-        const int ahead = std::min(NST - 2, nch - 1 - ch);
-        if (ahead >= 2)
-            wait_vm<2 * PER_STAGE>();
-        else if (ahead == 1)
-            wait_vm<PER_STAGE>();
-        else
-            wait_vm<0>();
-        lds_barrier();   // and every wave is done with chunk ch - 1's buffer
-        if (ch + NST - 1 < nch) issue(ch + NST - 1);
-        const float *as = lds + (ch % NST) * STAGE;
-        const float *bs = as + TSTAGE;
-        // the whole chunk's operands first (LDS reads return in order, so the
-        // products wait only for the reads they use), then the products
-        float fa[TK / 2][2], fb[TK / 2][MB];
-#pragma unroll
-        for (int s = 0; s < TK / 2; ++s) {
-            const int k = 2 * s + h;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) fa[s][m] = as[k * TLD + wr * 64 + m * 32 + li];
-#pragma unroll
-            for (int m = 0; m < MB; ++m) fb[s][m] = bs[k * TN + wc * (TN / 2) + m * 32 + li];
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
-#pragma unroll
-        for (int s = 0; s < TK / 2; ++s)
-            // D[n][m] += sum_k B(k, n) A(k, m): the tile transposed
-#pragma unroll
-            for (int ma = 0; ma < 2; ++ma)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[ma][mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[s][mb], fa[s][ma], acc[ma][mb], 0, 0, 0);
-    }
-
-    // W tile -= product; accumulator register 4g + b is column c + b of row r
-#pragma unroll
-    for (int ma = 0; ma < 2; ++ma)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r = wr * 64 + ma * 32 + li, c = wc * (TN / 2) + mb * 32 + 8 * g + 4 * h;
-                f32x4 x = cv[ma][mb][g];
-                x.x -= acc[ma][mb][4 * g + 0];
-                x.y -= acc[ma][mb][4 * g + 1];
-                x.z -= acc[ma][mb][4 * g + 2];
-                x.w -= acc[ma][mb][4 * g + 3];
-                float *dst = C + (int64_t)r * d_in + c;
-                if (full_tile) {
-                    *(f32x4 *)dst = x;
-                } else if (r < rows) {
-                    if (c + 3 < cols) {
-                        *(f32x4 *)dst = x;
-                    } else {
-                        if (c + 0 < cols) dst[0] = x.x;
-                        if (c + 1 < cols) dst[1] = x.y;
-                        if (c + 2 < cols) dst[2] = x.z;
-                    }
-                }
-            }
-}
-
-template <int TN>
-__global__ __launch_bounds__(256, 1) void trail_dma_kernel(QuantArgs a, int u_row0, int K, int c_begin, int c_end,
-                                                        int tiles_m) {
-    __shared__ __attribute__((aligned(16))) float lds[NST * DmaShape<TN>::STAGE];
-    trail_dma_tile<TN>(a, u_row0, K, c_begin, c_end, tiles_m, lds);
+    dma_tile_product<TN>(a.Wp + row0 * a.d_in + col0, a.d_in, rows, cols, a.E + row0, a.d_out,
+                         ((int64_t)K * a.d_out - row0) * 4, a.U + (int64_t)u_row0 * a.d_in + col0, a.d_in,
+                         ((int64_t)K * a.d_in - col0) * 4, K, DMA_SUB, lds);
 }
 
 int trail_cu_count() {
@@ -414,7 +241,7 @@ hipError_t trail_launch(const QuantArgs &a, int64_t u_row0, int64_t K, int64_t c
     const bool aligned = a.d_out % 4 == 0 && a.d_in % 4 == 0 && c_begin % 4 == 0 &&
                          reinterpret_cast<uintptr_t>(a.E) % 16 == 0 && reinterpret_cast<uintptr_t>(a.U) % 16 == 0 &&
                          reinterpret_cast<uintptr_t>(a.Wp) % 16 == 0 &&
-                         K * std::max(a.d_out, a.d_in) * 4 + (int64_t)TK * std::max(a.d_out, a.d_in) * 4 * NST < ((int64_t)1 << 31);
+                         K * std::max(a.d_out, a.d_in) * 4 + (int64_t)DK * std::max(a.d_out, a.d_in) * 4 * DNST < ((int64_t)1 << 31);
     if (aligned) {
         // 128-wide tiles, except that when they would leave a last round of
         // at most half the compute units, that round's whole column tiles go

@@ -144,9 +144,13 @@ def test_hessian_full_size_sampled_channels_down70b():
 # ---------------------------------------------------------------------------
 # stage 2 alone
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("d,act", [(1, False), (7, True), (128, False), (300, True), (520, False)])
-def test_inverse_factor_parity(d, act):
-    wl = synth.WORKLOADS["q_proj"].with_shape(200 + d, 8, d, max(4 * d, 256))
+# 8292: 65 blocks, the batched schedule (eight steps per far update, then a
+# ragged last block); fewer tokens than channels, so H is low-rank and the
+# damping carries its smallest eigenvalues.
+@pytest.mark.parametrize("d,act,n", [(1, False, None), (7, True, None), (128, False, None), (300, True, None),
+                                     (520, False, None), (8292, True, 2048)])
+def test_inverse_factor_parity(d, act, n):
+    wl = synth.WORKLOADS["q_proj"].with_shape(200 + d, 8, d, n or max(4 * d, 256))
     X = synth.make_x(wl)
     H32 = O.hessian([X], "bf16", d).astype(np.float32)       # the same fp32 H goes to both sides
     Hd = torch.from_numpy(H32).to(DEV)
