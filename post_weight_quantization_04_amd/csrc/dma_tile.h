@@ -8,9 +8,10 @@
 //   P(m, n) = sum_{k < K} A[k * lda + m] B[k * ldb + n]
 //
 // for one 128 x TN tile of C (row stride ldc): both operands are k-major,
-// contiguous along the tile's rows (A) and columns (B).  One work group per
-// compute unit; chunks of 32 k-rows move by 16-byte buffer loads through a
-// four-stage LDS ring, three chunks in flight while one is multiplied.  The
+// contiguous along the tile's rows (A) and columns (B).  Chunks of KC k-rows
+// move by 16-byte buffer loads through an NST-stage LDS ring, NST - 1 chunks
+// in flight while one is multiplied (by default 32 k-rows, four stages and
+// 128 KB: one work group per compute unit).  The
 // buffer resources end where the caller says the operand ends (normally at
 // k-row K), so the ragged last chunk reads zeros without a branch; rows and
 // columns past the tile's edge only feed entries that are not stored.
@@ -25,9 +26,8 @@ namespace gptq {
 namespace {
 
 constexpr int DT = 128;               // tile rows
-constexpr int DK = 32;                // k-rows per chunk
-constexpr int DSTAGE_A = DK * DT;     // one A chunk (floats)
-constexpr int DNST = 4;               // ring stages
+constexpr int DK = 32;                // default k-rows per chunk
+constexpr int DNST = 4;               // default ring stages
 
 enum DmaMode { DMA_SUB = 0, DMA_ADD = 1, DMA_SET = 2 };
 
@@ -56,36 +56,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const float *p, int64
 }
 
 // Tiles are 128 rows x TN columns (TN = 128 or 64).  Waves form a 2 x 2 grid
-// of 64 x TN/2 blocks (MB = TN/64 MFMA blocks across).
-template <int TN>
+// of 64 x TN/2 blocks (MB = TN/64 MFMA blocks across).  Each of the four
+// waves moves KC/4 k-rows of every chunk.
+template <int TN, int NST = DNST, int KC = DK>
 struct DmaShape {
+    static_assert(KC % 16 == 0 && NST >= 2, "chunk of whole 16-row groups, at least two stages");
     static constexpr int MB = TN / 64;                 // 32-column MFMA blocks per wave
-    static constexpr int BST = DK * TN;                // B chunk (floats)
-    static constexpr int STAGE = DSTAGE_A + BST;       // one ring stage: A chunk then B chunk
+    static constexpr int AST = KC * DT;                // A chunk (floats)
+    static constexpr int BST = KC * TN;                // B chunk (floats)
+    static constexpr int STAGE = AST + BST;            // one ring stage: A chunk then B chunk
+    static constexpr int RPW = KC / 4;                 // k-rows per wave per chunk
+    static constexpr int AINS = RPW / 2;               // A load instructions per wave (2 rows each)
     static constexpr int BROWS = 1024 / (TN * 4);      // B k-rows per 1 KB load instruction (2 or 4)
-    static constexpr int BINS = 8 / BROWS;             // B load instructions per wave per stage
-    static constexpr int PER_STAGE = 4 + BINS;         // vector-memory instructions per stage per wave
-    static constexpr int LDS_FLOATS = DNST * STAGE;
+    static constexpr int BINS = RPW / BROWS;           // B load instructions per wave per stage
+    static constexpr int PER_STAGE = AINS + BINS;      // vector-memory instructions per stage per wave
+    static constexpr int LDS_FLOATS = NST * STAGE;
 };
 
 typedef __attribute__((ext_vector_type(16))) float dma_f32x16;
 
 // One tile.  rows / cols: the tile's extent inside C (at most 128 / TN).
 // a_bytes / b_bytes: readable bytes from A / B (reads past them give zero).
-// lds: DmaShape<TN>::LDS_FLOATS floats, 16-byte aligned.
-template <int TN>
+// lds: DmaShape<TN, NST, KC>::LDS_FLOATS floats, 16-byte aligned.
+template <int TN, int NST = DNST, int KC = DK>
 __device__ __forceinline__ void dma_tile_product(float *C, int64_t ldc, int rows, int cols, const float *A, int64_t lda,
                                                  int64_t a_bytes, const float *B, int64_t ldb, int64_t b_bytes, int K,
                                                  int mode, float *lds) {
-    constexpr int MB = DmaShape<TN>::MB;
-    constexpr int STAGE = DmaShape<TN>::STAGE;
-    constexpr int BROWS = DmaShape<TN>::BROWS;
-    constexpr int BINS = DmaShape<TN>::BINS;
-    constexpr int PER_STAGE = DmaShape<TN>::PER_STAGE;
+    typedef DmaShape<TN, NST, KC> S;
+    constexpr int MB = S::MB;
+    constexpr int STAGE = S::STAGE;
+    constexpr int AST = S::AST;
+    constexpr int RPW = S::RPW;
+    constexpr int AINS = S::AINS;
+    constexpr int BROWS = S::BROWS;
+    constexpr int BINS = S::BINS;
+    constexpr int PER_STAGE = S::PER_STAGE;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wr = wave >> 1, wc = wave & 1, h = lane >> 5, li = lane & 31;
-    const int nch = (K + DK - 1) / DK;
+    const int nch = (K + KC - 1) / KC;
     // accumulator (ma, mb), register group g: C row wr*64 + ma*32 + li,
     // columns wc*TN/2 + mb*32 + 8g + 4h + [0, 4)
 
@@ -119,30 +128,30 @@ __device__ __forceinline__ void dma_tile_product(float *C, int64_t ldc, int rows
 
     const __amdgpu_buffer_rsrc_t ra = dma_rsrc(A, a_bytes);
     const __amdgpu_buffer_rsrc_t rb = dma_rsrc(B, b_bytes);
-    // wave w moves k-rows 8w .. 8w+7 of each chunk: A two rows per
-    // instruction (32 lanes x 16 bytes each), B BROWS rows per instruction
-    int offa[4], offb[BINS];
+    // wave w moves k-rows RPW w .. RPW w + RPW-1 of each chunk: A two rows
+    // per instruction (32 lanes x 16 bytes each), B BROWS rows per instruction
+    int offa[AINS], offb[BINS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) offa[q] = (int)(((8 * wave + 2 * q + h) * lda + 4 * li) * 4);
+    for (int q = 0; q < AINS; ++q) offa[q] = (int)(((RPW * wave + 2 * q + h) * lda + 4 * li) * 4);
     {
         const int lpr = TN / 4;   // lanes per B row
 #pragma unroll
         for (int q = 0; q < BINS; ++q)
-            offb[q] = (int)(((8 * wave + BROWS * q + lane / lpr) * ldb + 4 * (lane % lpr)) * 4);
+            offb[q] = (int)(((RPW * wave + BROWS * q + lane / lpr) * ldb + 4 * (lane % lpr)) * 4);
     }
     auto issue = [&](int st) {
-        dma_lds_char *buf = (dma_lds_char *)lds + (st % DNST) * STAGE * 4;
-        const int sa = (int)(st * DK * lda * 4), sb = (int)(st * DK * ldb * 4);
+        dma_lds_char *buf = (dma_lds_char *)lds + (st % NST) * STAGE * 4;
+        const int sa = (int)(st * KC * lda * 4), sb = (int)(st * KC * ldb * 4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (dma_lds_void_t *)(buf + (8 * wave + 2 * q) * DT * 4), 16,
+        for (int q = 0; q < AINS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (dma_lds_void_t *)(buf + (RPW * wave + 2 * q) * DT * 4), 16,
                                                      offa[q] + sa, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < BINS; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (dma_lds_void_t *)(buf + (DSTAGE_A + (8 * wave + BROWS * q) * TN) * 4), 16, offb[q] + sb, 0, 0, 0);
+                rb, (dma_lds_void_t *)(buf + (AST + (RPW * wave + BROWS * q) * TN) * 4), 16, offb[q] + sb, 0, 0, 0);
     };
-    for (int st = 0; st < DNST - 1 && st < nch; ++st) issue(st);
+    for (int st = 0; st < NST - 1 && st < nch; ++st) issue(st);
 
     dma_f32x16 acc[2][MB];
 #pragma unroll
@@ -151,7 +160,8 @@ __device__ __forceinline__ void dma_tile_product(float *C, int64_t ldc, int rows
         for (int mb = 0; mb < MB; ++mb) acc[ma][mb] = dma_f32x16{};
     for (int ch = 0; ch < nch; ++ch) {
         // chunk ch landed: the chunks issued after it may stay in flight
-        const int ahead = std::min(DNST - 2, nch - 1 - ch);
+        const int ahead = std::min(NST - 2, nch - 1 - ch);
+        static_assert(NST <= 4, "waits written out for up to two chunks ahead");
         if (ahead >= 2)
             dma_wait_vm<2 * PER_STAGE>();
         else if (ahead == 1)
@@ -159,14 +169,14 @@ __device__ __forceinline__ void dma_tile_product(float *C, int64_t ldc, int rows
         else
             dma_wait_vm<0>();
         dma_lds_barrier();   // and every wave is done with chunk ch - 1's buffer
-        if (ch + DNST - 1 < nch) issue(ch + DNST - 1);
-        const float *as = lds + (ch % DNST) * STAGE;
-        const float *bs = as + DSTAGE_A;
+        if (ch + NST - 1 < nch) issue(ch + NST - 1);
+        const float *as = lds + (ch % NST) * STAGE;
+        const float *bs = as + AST;
         // the whole chunk's operands first (LDS reads return in order, so the
         // products wait only for the reads they use), then the products
-        float fa[DK / 2][2], fb[DK / 2][MB];
+        float fa[KC / 2][2], fb[KC / 2][MB];
 #pragma unroll
-        for (int s = 0; s < DK / 2; ++s) {
+        for (int s = 0; s < KC / 2; ++s) {
             const int k = 2 * s + h;
 #pragma unroll
             for (int m = 0; m < 2; ++m) fa[s][m] = as[k * DT + wr * 64 + m * 32 + li];
@@ -175,7 +185,7 @@ __device__ __forceinline__ void dma_tile_product(float *C, int64_t ldc, int rows
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
 #pragma unroll
-        for (int s = 0; s < DK / 2; ++s)
+        for (int s = 0; s < KC / 2; ++s)
             // D[n][m] += sum_k B(k, n) A(k, m): the tile transposed
 #pragma unroll
             for (int ma = 0; ma < 2; ++ma)

@@ -9,11 +9,11 @@
 // pending blocks' errors stacked (the same sum, fewer passes over W).
 //
 // Main kernel (trail_dma_kernel, 16-byte aligned shapes): one work group per
-// 128 x 128 tile and one group per compute unit, the operand chunks moved
+// 128 x 128 tile and two groups per compute unit, the operand chunks moved
 // from global memory straight into LDS by 16-byte buffer loads through a
-// four-stage ring, three chunks in flight while one is multiplied, so that a
-// tile runs at the matrix cores' rate even when it has its unit to itself
-// (a launch's last, partial round).  The buffer resources end at row K of E
+// four-stage ring of 16 k-rows, three chunks in flight while one is
+// multiplied, so that a tile keeps the matrix cores busy even when it has its
+// unit to itself (a launch's last, partial round).  The buffer resources end at row K of E
 // and U, so the ragged last chunk reads zeros without a branch; rows and
 // columns past the tile's edge only feed entries that are not stored.  The
 // tile body (dma_tile.h) is shared with the factorization's far update.
@@ -206,16 +206,21 @@ __global__ __launch_bounds__(256, 2) void trail_kernel(QuantArgs a, int u_row0, 
 // tile origins) and K * max(d_out, d_in) * 4 < 2^31.
 // A(k, m) = E[k][row0 + m] and B(k, n) = U[u_row0 + k][col0 + n] for k < K:
 // the buffer resources end at row K of E and U.
+// Two groups per compute unit (a 64 KB ring each: four stages of 16 k-rows),
+// so that one group's tile start overlaps the other's products (against one
+// group per unit with four stages of 32 k-rows: q_proj's far launches
+// 0.54 -> 0.50 ms per layer, down_proj's 4.42 -> 3.85 ms).
+constexpr int TRAIL_NST = 4, TRAIL_KC = 16;
 template <int TN>
-__global__ __launch_bounds__(256, 1) void trail_dma_kernel(QuantArgs a, int u_row0, int K, int c_begin, int c_end,
+__global__ __launch_bounds__(256, 2) void trail_dma_kernel(QuantArgs a, int u_row0, int K, int c_begin, int c_end,
                                                         int tiles_m) {
-    __shared__ __attribute__((aligned(16))) float lds[DmaShape<TN>::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[DmaShape<TN, TRAIL_NST, TRAIL_KC>::LDS_FLOATS];
     const int t = blockIdx.x;
     const int64_t row0 = (int64_t)(t % tiles_m) * TT;
     const int64_t col0 = (int64_t)c_begin + (int64_t)(t / tiles_m) * TN;
     const int rows = (int)std::min<int64_t>(TT, a.d_out - row0);
     const int cols = (int)std::min<int64_t>(TN, c_end - col0);
-    dma_tile_product<TN>(a.Wp + row0 * a.d_in + col0, a.d_in, rows, cols, a.E + row0, a.d_out,
+    dma_tile_product<TN, TRAIL_NST, TRAIL_KC>(a.Wp + row0 * a.d_in + col0, a.d_in, rows, cols, a.E + row0, a.d_out,
                          ((int64_t)K * a.d_out - row0) * 4, a.U + (int64_t)u_row0 * a.d_in + col0, a.d_in,
                          ((int64_t)K * a.d_in - col0) * 4, K, DMA_SUB, lds);
 }
