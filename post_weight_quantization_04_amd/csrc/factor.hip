@@ -569,27 +569,33 @@ __device__ __forceinline__ void signal_count(int32_t *cnt) {
 // the diagonal of a diagonal quadrant) on fp32 MFMA, computed transposed
 // (lane (h, li), register 4a+b: row li, column 8a+4h+b).  The products run
 // over k in any order as long as both operands agree, so lane half h
-// supplies k = 64h + s at step s: every lane reads its two P rows' 64 values
-// as 16-byte loads straight into registers, all issued together, and the
-// 64 products then run back to back.  Rows past the block read a clamped
-// row and only feed entries that are not stored.
+// supplies k = 64h + s at step s.  The two 64-row blocks of P (one for a
+// diagonal quadrant) go to LDS first with coalesced 16-byte loads (each
+// 32-lane half reads 512 contiguous bytes of one row; loaded per lane along
+// its own row, every load instruction touched 64 cache lines and the 32 of
+// them took 3-6 k cycles to issue), rows padded to 132 floats so that the
+// 16-byte fragment reads, one row per lane, hit distinct banks; then the 64
+// products run back to back.  Rows past the block repeat the last row and
+// only feed entries that are not stored.
+constexpr int QLD = NB + 4;                                // LDS row stride of the staged P rows
+constexpr int QSTAGE = 2 * 64 * QLD;                       // both 64-row blocks (floats)
 __device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, int n0, int rows, int q,
-                                              const float *__restrict__ P) {
+                                              const float *__restrict__ P, float *lds) {
     const int qa = (q >= 1) ? 1 : 0, qb = (q == 2) ? 1 : 0;
     const int ra = 64 * qa, rb = 64 * qb;
-    if (ra >= rows) return;   // the block has no such quadrant
+    if (ra >= rows) return;   // the block has no such quadrant (uniform over the group)
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, li = lane & 31;
     const int sa = wave >> 1, sb = wave & 1;
-    if (qa == qb && sa < sb) return;                       // above the diagonal: not needed
+    const bool active = !(qa == qb && sa < sb);            // above the diagonal: not needed
     const int r = ra + 32 * sa + li;                       // this lane's row of the tile (P_a row)
     const int cb = rb + 32 * sb;                           // the sub-block's first column
     float *Crow = R + (int64_t)(n0 + r) * d + n0;
-    // acc = -C, then acc += P_b P_a^T (transposed), C = -acc.  A full tile
-    // (every step but the last) loads C without guards, before the operands,
-    // so that both sets of loads are in flight together.
+    // acc = -C, then acc += P_b P_a^T (transposed), C = -acc.  The C loads go
+    // out first (a full tile without guards), then the P rows, so that both
+    // sets are in flight together.
     f32x4 cv[4];
-    if (rows == NB) {
+    if (rows == NB && active) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) cv[a] = *(const f32x4 *)(Crow + cb + 8 * a + 4 * h);
     } else {
@@ -597,7 +603,7 @@ __device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, 
         for (int a = 0; a < 4; ++a) {
             const int c = cb + 8 * a + 4 * h;
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (r < rows) {
+            if (active && r < rows) {
                 if (c + 3 < rows) {
                     x = *(const f32x4 *)(Crow + c);
                 } else {
@@ -609,15 +615,39 @@ __device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, 
             cv[a] = x;
         }
     }
-    const float *pa = P + (int64_t)min(r, rows - 1) * NB + 64 * h;
-    const float *pb = P + (int64_t)min(cb + li, rows - 1) * NB + 64 * h;
+    // stage P rows ra.. (block 0) and rb.. (block 1, off-diagonal quadrant
+    // only): piece t + 256 i is row ((t + 256 i) / 32) % 64 of block
+    // (t + 256 i) / 2048, 16-byte column group t % 32
+    const int nblkrows = (qa == qb) ? 1 : 2;
+    {
+        f32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int piece = tid + 256 * i;
+            const int blk = piece >> 11, row = (piece >> 5) & 63, c4 = 4 * (piece & 31);
+            const int src_row = min((blk ? rb : ra) + row, rows - 1);
+            v[i] = (blk < nblkrows) ? *(const f32x4 *)(P + (int64_t)src_row * NB + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int piece = tid + 256 * i;
+            const int blk = piece >> 11, row = (piece >> 5) & 63, c4 = 4 * (piece & 31);
+            if (blk < nblkrows) *(f32x4 *)(lds + (blk * 64 + row) * QLD + c4) = v[i];
+        }
+    }
+    __syncthreads();
+    if (!active) return;
+    // A row 32 sa + li of block 0; B row 32 sb + li of block 1 (block 0 for
+    // a diagonal quadrant, whose two blocks are the same rows)
+    const float *pa = lds + (32 * sa + li) * QLD + 64 * h;
+    const float *pb = lds + ((qa == qb ? 0 : 64) + 32 * sb + li) * QLD + 64 * h;
     f32x4 av[16], bv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         av[j] = *(const f32x4 *)(pa + 4 * j);
         bv[j] = *(const f32x4 *)(pb + 4 * j);
     }
-    // every load goes out before the first product (one memory latency)
+    // every read goes out before the first product
     __builtin_amdgcn_sched_barrier(0);
     f32x16 acc;
 #pragma unroll
@@ -664,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
                                                      const float *__restrict__ dinv_k,
                                                      float *__restrict__ dinv_next, int32_t *__restrict__ info,
                                                      int target) {
-    __shared__ __attribute__((aligned(16))) float lds[4 * GSTAGE];
+    __shared__ __attribute__((aligned(16))) float lds[std::max(4 * GSTAGE, QSTAGE)];
     __shared__ __attribute__((aligned(16))) float bc[64];
     const int k0 = k * NB, kb = (int)std::min<int64_t>(NB, d - k0), k1 = k0 + kb;
     const int b = blockIdx.x;
@@ -672,7 +702,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
         const int n0 = (k + 1) * NB;
         const int rows = (int)std::min<int64_t>(NB, d - n0);
         if (b > 0) {
-            diag_quadrant(R, d, n0, rows, b - 1, panel + (int64_t)(n0 - k1) * NB);
+            diag_quadrant(R, d, n0, rows, b - 1, panel + (int64_t)(n0 - k1) * NB, lds);
             signal_count(info + 1);
             return;
         }
