@@ -10,11 +10,12 @@
 // for one 128 x TN tile of C (row stride ldc): both operands are k-major,
 // contiguous along the tile's rows (A) and columns (B).  Chunks of KC k-rows
 // move by 16-byte buffer loads through an NST-stage LDS ring, NST - 1 chunks
-// in flight while one is multiplied (by default 32 k-rows, four stages and
-// 128 KB: one work group per compute unit).  The
-// buffer resources end where the caller says the operand ends (normally at
-// k-row K), so the ragged last chunk reads zeros without a branch; rows and
-// columns past the tile's edge only feed entries that are not stored.
+// in flight while one is multiplied (by default 32 k-rows and four stages,
+// 128 KB: one work group per compute unit; both users take 16 k-rows, 64 KB,
+// two groups per unit).  The buffer resources end where the caller says the
+// operand ends (normally at k-row K), so the ragged last chunk reads zeros
+// without a branch; rows and columns past the tile's edge only feed entries
+// that are not stored.
 // Requires lda, ldb, ldc and the operand and tile origins to be 16-byte
 // aligned, and K * max(lda, ldb) * 4 + 4 chunks < 2^31 (32-bit offsets).
 #pragma once
