@@ -416,6 +416,46 @@ __device__ __forceinline__ void gemm_strip(f32x16 &acc, const float *A, int64_t 
         cw.store(wide + buf * WST, ROWS ? 1.f : alpha);
         cn.store(narrow + buf * NST, ROWS ? alpha : 1.f);
     };
+    if (full && K == NB) {
+        // full strip, full K: all four chunks' loads go out unguarded at the
+        // start (one memory latency), then pass through the two LDS buffers
+        constexpr int MAXC = NB / GK;
+        Chunk<ROWS ? B_KCONTIG : A_KCONTIG> xw[MAXC];
+        NChunk<ROWS ? A_KCONTIG : B_KCONTIG> xn[MAXC];
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            if (ROWS) {
+                xn[c].load(A, lda, c * GK, rows, K, true);
+                xw[c].load(B, ldb, c * GK, cols, K, true);
+            } else {
+                xw[c].load(A, lda, c * GK, rows, K, true);
+                xn[c].load(B, ldb, c * GK, cols, K, true);
+            }
+        }
+        xw[0].store(wide, ROWS ? 1.f : alpha);
+        xn[0].store(narrow, ROWS ? alpha : 1.f);
+        __syncthreads();
+#pragma unroll
+        for (int ch = 0; ch < MAXC; ++ch) {
+            const int buf = ch & 1;
+            const float *ws = wide + buf * WST;
+            const float *ns = narrow + buf * NST;
+#pragma unroll
+            for (int s = 0; s < GK / 2; ++s) {
+                const int row = 2 * s + h;
+                const float fw = ws[row * GLD + wave * 32 + li];
+                const float fn = ns[row * SLD + li];
+                if (ROWS) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fw, fn, acc, 0, 0, 0);
+                else acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fn, fw, acc, 0, 0, 0);
+            }
+            if (ch + 1 < MAXC) {
+                xw[ch + 1].store(wide + (buf ^ 1) * WST, ROWS ? 1.f : alpha);
+                xn[ch + 1].store(narrow + (buf ^ 1) * NST, ROWS ? alpha : 1.f);
+            }
+            __syncthreads();
+        }
+        return;
+    }
     load(0, full && GK <= K);
     store(0);
     __syncthreads();
