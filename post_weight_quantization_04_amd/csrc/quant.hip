@@ -418,9 +418,10 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
         //   W[16 rows][j] -= sum_{k < near_k} En[k][row] U[near_row0 + k][b + j]
         // as 16 x 16 tiles on v_mfma_f32_16x16x4_f32 (A[i][k] at lane i + 16k,
         // B[k][j] at lane j + 16k, D[i][j] at lane 16 (i/4) + j, register
-        // i % 4).  Wave w takes column tiles w and w + 4 (then w + 8, w + 12
-        // for blocks past 128 columns); k goes in batches of 64 whose
-        // operand loads (from L2) are all issued before their products.
+        // i % 4).  Wave w takes column tiles w, w + 4, w + 8 and w + 12 (those
+        // inside the block), all four accumulated over one pass of k, so each
+        // error value is loaded once; k goes in batches of 32 whose operand
+        // loads (from L2) go out one batch ahead of the products.
         const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
         // every load reads an address clamped into range and the value is
         // zeroed afterwards, so that the loads carry no branches and go out
@@ -430,42 +431,60 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
         const float *ep = a.En + (ra_ok ? ra : d_out - 1);              // En[k][ra]
         const float *up = a.U + a.near_row0 * d_in + b;                 // U[near_row0 + k][b + j]
         const int nk = a.near_k;
-        for (int jp = 16 * wave; jp < nb; jp += 128) {
-            const int j1 = jp + 64;                                     // second tile of the pair
-            const bool c0_ok = jp + li < nb, c1_ok = j1 + li < nb;
-            const int cc0 = c0_ok ? jp + li : nb - 1, cc1 = c1_ok ? j1 + li : nb - 1;
-            for (int k0 = 0; k0 < nk; k0 += 64) {
-                float ea[16], ub0[16], ub1[16];
+        constexpr int NT = 4, KB = 32, KT = KB / 4;
+        int cc[NT];
+        bool c_ok[NT], t_on[NT];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const int k = k0 + 4 * t + lk;
-                    const bool k_ok = k < nk;
-                    const int64_t kc = k_ok ? k : nk - 1;
-                    const float e = ep[kc * d_out];
-                    const float u0 = up[kc * d_in + cc0];
-                    const float u1 = up[kc * d_in + cc1];
-                    ea[t] = (k_ok && ra_ok) ? -e : 0.f;
-                    ub0[t] = (k_ok && c0_ok) ? u0 : 0.f;
-                    ub1[t] = (k_ok && c1_ok) ? u1 : 0.f;
-                }
-                f32x4 acc0, acc1;
+        for (int t = 0; t < NT; ++t) {
+            const int jt = 16 * wave + 64 * t;
+            t_on[t] = jt < nb;
+            c_ok[t] = jt + li < nb;
+            cc[t] = c_ok[t] ? jt + li : nb - 1;
+        }
+        f32x4 acc[NT];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    acc0[r] = Wl[(4 * lk + r) * LW + jp + li];
-                    acc1[r] = (j1 < Bp) ? Wl[(4 * lk + r) * LW + j1 + li] : 0.f;
-                }
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub0[t], acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub1[t], acc1, 0, 0, 0);
-                }
+            for (int r = 0; r < 4; ++r) acc[t][r] = t_on[t] ? Wl[(4 * lk + r) * LW + 16 * wave + 64 * t + li] : 0.f;
+        float ea[KT], ub[NT][KT];
+        auto load = [&](int k0, float (&e_)[KT], float (&u_)[NT][KT]) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    Wl[(4 * lk + r) * LW + jp + li] = acc0[r];
-                    if (j1 < Bp) Wl[(4 * lk + r) * LW + j1 + li] = acc1[r];
-                }
+            for (int q = 0; q < KT; ++q) {
+                const int k = k0 + 4 * q + lk;
+                const int64_t kc = k < nk ? k : nk - 1;
+                e_[q] = ep[kc * d_out];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) u_[t][q] = up[kc * d_in + cc[t]];
+            }
+        };
+        load(0, ea, ub);
+        for (int k0 = 0; k0 < nk; k0 += KB) {
+            float en[KT], un[NT][KT];
+            if (k0 + KB < nk) load(k0 + KB, en, un);
+            // zero what lies past the matrix, after the loads are in flight
+#pragma unroll
+            for (int q = 0; q < KT; ++q) {
+                const bool k_ok = k0 + 4 * q + lk < nk;
+                ea[q] = (k_ok && ra_ok) ? -ea[q] : 0.f;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) ub[t][q] = (k_ok && c_ok[t]) ? ub[t][q] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < KT; ++q)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[q], ub[t][q], acc[t], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < KT; ++q) {
+                ea[q] = en[q];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) ub[t][q] = un[t][q];
             }
         }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (t_on[t])
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Wl[(4 * lk + r) * LW + 16 * wave + 64 * t + li] = acc[t][r];
         __syncthreads();
     }
 
