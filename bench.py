@@ -131,7 +131,7 @@ def main():
                     help="accepted for compatibility (the timed steps always run without per-stage events)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the quantizer runs on a single MI355X and this build has no "
+        print("bench.py measures one GPU only: the quantizer runs on a single MI355X and has no "
               "multi-GPU path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
