@@ -67,6 +67,51 @@ def test_quantizer_properties():
 
 
 # --------------------------------------------------------------------------
+# damping constant and the timing of group parameters: hand-worked values
+# (tests/golden/damping_and_group_timing.json holds the derivations)
+# --------------------------------------------------------------------------
+def _golden_dg():
+    return json.load(open(os.path.join(GOLDEN, "damping_and_group_timing.json")))
+
+
+def test_damping_hand_examples():
+    f = _golden_dg()
+    c = f["damping_diagonal"]
+    H = np.diag(c["diag_H"])
+    assert O.damping(H, c["damp"]) == pytest.approx(c["lambda"], rel=1e-15)
+    W = np.zeros((1, 4))
+    r = O.gptq(W, H, 4, -1, 4, c["damp"], False)
+    assert r["lam"] == pytest.approx(c["lambda"], rel=1e-15)
+    assert np.allclose(np.diag(r["U"]), c["U_diag"], rtol=1e-14, atol=0)
+    c = f["damping_2x2"]
+    H = np.array(c["H"])
+    r = O.gptq(np.zeros((1, 2)), H, 4, -1, 2, c["damp"], False)
+    assert r["lam"] == pytest.approx(c["lambda"], rel=1e-15)
+    assert np.allclose(r["U"], c["U"], rtol=1e-14, atol=1e-16)
+    # the same U from the second route on the hand-damped matrix
+    Hd = H + c["lambda"] * np.eye(2)
+    assert np.allclose(O.inverse_cholesky_upper_reverse(Hd), c["U"], rtol=1e-14, atol=1e-16)
+
+
+@pytest.mark.parametrize("B", [2, 4])
+def test_group_parameters_from_compensated_values(B):
+    c = _golden_dg()["group_timing"]
+    H = np.array(c["H"])
+    W = np.array(c["W"])
+    r = O.gptq(W, H, c["bits"], c["group_size"], B, c["damp"], False)
+    assert np.allclose(r["U"], c["U_chosen"], rtol=0, atol=1e-13)
+    assert r["codes"].tolist() == c["codes"]
+    assert np.allclose(r["scales"], c["scales"], rtol=1e-12, atol=0)
+    assert np.array_equal(r["zeros"], np.array(c["zeros"]))
+    assert np.allclose(r["E"], c["E"], rtol=0, atol=1e-13)
+    assert np.allclose(r["w_hat"], c["w_hat"], rtol=0, atol=1e-13)
+    # the column-by-column form with explicit inverses of the remaining set
+    nv = O.obq_naive(W, H, c["bits"], c["group_size"], c["damp"], False)
+    assert nv["codes"].tolist() == c["codes"]
+    assert np.allclose(nv["w_hat"], c["w_hat"], rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # P1: H proportional to I  =>  no compensation  =>  plain per-group RTN
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("bits,g,B", [(4, 8, 8), (4, 8, 16), (3, 4, 12), (2, -1, 5), (4, 16, 32)])
