@@ -104,8 +104,10 @@ def check_layer(W0: np.ndarray, H_ref: np.ndarray, bits: int, group_size: int, b
                 damp: float, act_order: bool, qpacked: np.ndarray, scales: np.ndarray,
                 zeros: np.ndarray, perm: np.ndarray, window: float = 1e-4,
                 exempt_frac: float = 1e-3, scale_rel: float = 1e-3, loss_rel: float = 5e-3,
-                ref_run: dict | None = None) -> dict:
-    """Full parity verdict for one layer.  W0: float64 [d_out, d_in] original order."""
+                ref_run: dict | None = None, U=None) -> dict:
+    """Full parity verdict for one layer.  W0: float64 [d_out, d_in] original order.
+    U: optional inverse factor from this package's oracle for H_ref in the
+    candidate's order and this damping (large layers compute it once)."""
     W0 = np.asarray(W0, dtype=np.float64)
     d_out, d_in = W0.shape
     g = O._eff_group(d_in, group_size)
@@ -126,18 +128,26 @@ def check_layer(W0: np.ndarray, H_ref: np.ndarray, bits: int, group_size: int, b
 
     fol = _Follow(codes, zeros, maxq, window)
     run = O.gptq(W0, H_ref, bits, group_size, block_size, damp, act_order, perm=np.asarray(perm),
-                 decide_code=fol.code, decide_zero=fol.zero)
+                 decide_code=fol.code, decide_zero=fol.zero, U=U)
     total = codes.size + zeros.size
     res.update(exempt_codes=fol.exempt_codes, exempt_zeros=fol.exempt_zeros,
                mismatch_codes=fol.mism_codes, mismatch_zeros=fol.mism_zeros,
                exempt_frac=(fol.exempt_codes + fol.exempt_zeros) / max(total, 1), worst=fol.worst)
+    # how close the oracle's own pre-round values came to a rounding boundary
+    # (distance to the nearest half-integer, code units) where both sides agree
+    dist = np.abs(run["t"] - np.floor(run["t"]) - 0.5)
+    res["min_boundary_dist"] = float(dist.min()) if dist.size else 0.0
+    res["within_1e-3_of_boundary"] = int(np.count_nonzero(dist < 1e-3))
     with np.errstate(divide="ignore", invalid="ignore"):
         srel = np.abs(scales - run["scales"]) / np.abs(run["scales"])
     res["scale_max_rel"] = float(np.nanmax(srel)) if srel.size else 0.0
 
     # loss against the oracle's own, unfollowed run
     if ref_run is None:
-        ref_run = O.gptq(W0, H_ref, bits, group_size, block_size, damp, act_order)
+        own = O.act_order_perm(H_ref) if act_order else np.arange(d_in)
+        same = np.array_equal(own, np.asarray(perm))     # then the factor is the same one
+        ref_run = O.gptq(W0, H_ref, bits, group_size, block_size, damp, act_order,
+                         U=run["U"] if same else None)
     W_ref = O.dequantize(ref_run["codes"], ref_run["scales"], ref_run["zeros"], ref_run["perm"], g)
     W_cand = O.dequantize(codes, scales, zeros, perm, g)
     l_ref = O.proxy_loss(W0, W_ref, H_ref)

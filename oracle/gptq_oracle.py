@@ -52,6 +52,7 @@ design notes of this repository):
 from __future__ import annotations
 
 import numpy as np
+import scipy.linalg
 
 __all__ = [
     "widen", "hessian", "act_order_perm", "damping", "inverse_cholesky_upper",
@@ -106,10 +107,14 @@ def inverse_cholesky_upper(Hd: np.ndarray) -> np.ndarray:
     Raises numpy.linalg.LinAlgError when H_d is not positive definite.
     """
     L = np.linalg.cholesky(Hd)
-    d = Hd.shape[0]
-    Linv = np.linalg.solve(L, np.eye(d))          # triangular system solved densely
+    Linv, info = scipy.linalg.lapack.dtrtri(L, lower=1)     # L^-1 (LAPACK triangular inverse)
+    if info != 0:
+        raise np.linalg.LinAlgError("singular Cholesky factor")
+    del L
     Hinv = Linv.T @ Linv
-    Hinv = 0.5 * (Hinv + Hinv.T)
+    del Linv
+    Hinv += Hinv.T
+    Hinv *= 0.5
     return np.linalg.cholesky(Hinv).T
 
 
@@ -118,11 +123,16 @@ def inverse_cholesky_upper_reverse(Hd: np.ndarray) -> np.ndarray:
 
     With J the reversal, J H_d J = L' L'^T gives H_d = V V^T, V = J L' J upper;
     then U = V^-1 (upper with positive diagonal, so equal to the plain route's
-    U by uniqueness of the Cholesky factor).
+    U by uniqueness of the Cholesky factor).  It costs a quarter of the plain
+    route's flops, so the large parity tests take their factor from here.
     """
-    Lr = np.linalg.cholesky(Hd[::-1, ::-1])
-    V = Lr[::-1, ::-1]
-    return np.linalg.solve(V, np.eye(Hd.shape[0]))
+    Lr = np.linalg.cholesky(np.ascontiguousarray(Hd[::-1, ::-1]))
+    V = np.ascontiguousarray(Lr[::-1, ::-1])
+    del Lr
+    U, info = scipy.linalg.lapack.dtrtri(V, lower=0)          # V^-1 (LAPACK triangular inverse)
+    if info != 0:
+        raise np.linalg.LinAlgError("singular Cholesky factor")
+    return U
 
 
 # ----------------------------------------------------------------------------
@@ -169,7 +179,7 @@ def _eff_group(d_in: int, group_size: int) -> int:
 # ----------------------------------------------------------------------------
 def gptq(W0: np.ndarray, H: np.ndarray, bits: int, group_size: int, block_size: int,
          damp: float, act_order: bool, perm=None, decide_code=None, decide_zero=None,
-         on_column=None) -> dict:
+         on_column=None, U=None) -> dict:
     """GPTQ on one layer, float64.
 
     W0: [d_out, d_in] values (float64); H: [d_in, d_in] undamped Hessian.
@@ -180,6 +190,8 @@ def gptq(W0: np.ndarray, H: np.ndarray, bits: int, group_size: int, block_size: 
           follow the other side at exact rounding ties); they must return
           arrays of the same shape.
     on_column(k, W): optional observer called after column k is done.
+    U: optional inverse factor already computed by this module for the same
+          H, order and damping (the parity checker's two runs share one).
 
     Returns a dict; every per-column array is in processing order:
       codes [d_out, d_in] int, scales/zeros [n_groups, d_out], perm [d_in],
@@ -201,10 +213,12 @@ def gptq(W0: np.ndarray, H: np.ndarray, bits: int, group_size: int, block_size: 
         perm = act_order_perm(H) if act_order else np.arange(d_in)
     perm = np.asarray(perm, dtype=np.int64)
     W = W0[:, perm].copy()
-    Hp = H[np.ix_(perm, perm)]
     lam = damping(H, damp)
-    Hd = Hp + lam * np.eye(d_in)
-    U = inverse_cholesky_upper(Hd)
+    if U is None:
+        Hd = H[np.ix_(perm, perm)]
+        Hd[np.diag_indices(d_in)] += lam
+        U = inverse_cholesky_upper(Hd)
+        del Hd
 
     G = (d_in + g - 1) // g
     codes = np.zeros((d_out, d_in), dtype=np.int64)

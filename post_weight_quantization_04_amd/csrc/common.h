@@ -100,6 +100,7 @@ struct QuantArgs {
     float *zeros;          // [G][d_out]
     int64_t d_out, d_in;
     int bits, group, block;   // group: effective group size (d_in when one group)
+    int ring_ok;           // the launch's LDS holds the near-update ring (set by the launcher)
 };
 size_t quant_lds_bytes(int block);
 // blocks [b0 + t*B, min(b0 + (t+1)*B, d_in)) for t < nblocks, one launch

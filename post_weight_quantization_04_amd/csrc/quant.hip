@@ -406,7 +406,7 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
     if (tid < Bp) rbl[tid] = uidx(tid, 0, Bp);
     __syncthreads();
 
-    const bool near_fast = nb == 128 && d_in % 4 == 0 && d_out % 4 == 0 && b % 4 == 0 &&
+    const bool near_fast = nb == 128 && a.ring_ok && d_in % 4 == 0 && d_out % 4 == 0 && b % 4 == 0 &&
                            a.near_k * std::max(d_in, d_out) * 4 + (int64_t)NSTG * NCH * std::max(d_in, d_out) * 4 <
                                ((int64_t)1 << 31);
     if (a.near_k > 0 && near_fast) {
@@ -628,6 +628,17 @@ size_t quant_lds_bytes(int block) {
     return sizeof(float) * (base + (block == 128 ? (size_t)NRING : 0));
 }
 
+// LDS of a launch over blocks of width B from b0 (nblocks of them): every
+// block but the last is B wide, the last may be narrower.  A 128-wide last
+// block after wider ones needs the near-update ring, which can take more
+// than the first block's staging (154944 bytes against 152896 at B = 256),
+// so the launch takes the larger of the two.
+static size_t quant_launch_lds(int64_t d_in, int64_t b0, int nblocks, int64_t B) {
+    const int w_first = (int)std::min<int64_t>(B, d_in - b0);
+    const int w_last = (int)std::min<int64_t>(B, d_in - (b0 + (int64_t)(nblocks - 1) * B));
+    return std::max(quant_lds_bytes(w_first), quant_lds_bytes(w_last));
+}
+
 int quant_cu_count() {
     static int cached = 0;
     if (cached == 0) {
@@ -654,14 +665,24 @@ hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64
     }
     if (B < 1 || B > 256 || nblocks < 1 || b0 + (nblocks - 1) * B >= a.d_in || b0 < a.near_row0)
         return hipErrorInvalidValue;   // the kernel stages at most 256 columns per block
-    const size_t lds = quant_lds_bytes((int)std::min<int64_t>(B, a.d_in - b0));   // the widest block is the first
     const unsigned grid = (unsigned)cdiv(a.d_out, QROWS);
+    // ring_ok: the allocation holds the near-update ring after a 128-wide
+    // block's staging (the kernel takes the ring only then)
+    const size_t ring_need = quant_lds_bytes(128);
     if ((int64_t)grid <= quant_cu_count()) {
-        quant_block_kernel<true><<<grid, 256, lds, st>>>(a, (int)b0, nblocks, (int)B);
+        const size_t lds = quant_launch_lds(a.d_in, b0, nblocks, B);
+        if (lds > 160 * 1024) return hipErrorInvalidValue;
+        QuantArgs ar = a;
+        ar.ring_ok = lds >= ring_need;
+        quant_block_kernel<true><<<grid, 256, lds, st>>>(ar, (int)b0, nblocks, (int)B);
         return hipGetLastError();
     }
     for (int t = 0; t < nblocks; ++t) {
-        quant_block_kernel<false><<<grid, 256, lds, st>>>(a, (int)(b0 + t * B), 1, (int)B);
+        const size_t lds = quant_launch_lds(a.d_in, b0 + t * B, 1, B);
+        if (lds > 160 * 1024) return hipErrorInvalidValue;
+        QuantArgs ar = a;
+        ar.ring_ok = lds >= ring_need;
+        quant_block_kernel<false><<<grid, 256, lds, st>>>(ar, (int)(b0 + t * B), 1, (int)B);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

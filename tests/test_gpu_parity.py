@@ -114,8 +114,6 @@ def test_hessian_full_size_sampled_channels():
 
 
 @pytest.mark.slow
-@pytest.mark.skipif(os.environ.get("GPTQ_FULL_PARITY") != "1",
-                    reason="full-size down70b Hessian is opt-in (GPTQ_FULL_PARITY=1): 7.5 GB of X generated on the host")
 def test_hessian_full_size_sampled_channels_down70b():
     """The largest workload (131072 x 28672 bf16, log-normal channel scales)
     in the benchmark's launch configuration; a sampled channel sub-block that
@@ -184,7 +182,7 @@ def test_not_positive_definite_is_reported():
 # ---------------------------------------------------------------------------
 # stages 1-5 end to end
 # ---------------------------------------------------------------------------
-# (workload, tag, d_out, d_in, n, bits, group, block, act_order)
+# (workload, tag, d_out, d_in, n, bits, group, block, act_order[, damp])
 LAYER_CASES = [
     ("toy", 1, 256, 512, 2048, 4, 128, 128, False),            # the full toy workload
     ("q_proj", 301, 200, 640, 4096, 4, 128, 128, False),       # ragged rows, five blocks
@@ -200,6 +198,13 @@ LAYER_CASES = [
     ("q_proj", 311, 40, 1536, 3000, 4, 512, 512, False),       # groups of 512 over two 256-column internal blocks
     ("down_proj", 312, 24, 2304, 3000, 4, 768, 768, True),     # groups of 768 over three internal blocks
     ("q_proj", 314, 4200, 384, 2048, 4, 128, 128, False),      # more row groups than CUs: one launch per block
+    ("down70b", 315, 64, 384, 2048, 4, 128, 256, False),       # a 128-wide last block after a 256-wide one
+    ("q_proj", 316, 48, 320, 2048, 4, 64, 192, False),         # the same after a 192-wide block
+    ("q_proj", 321, 4100, 384, 2048, 4, 128, 256, False),      # ... with one launch per block
+    ("q_proj", 317, 64, 1300, 3000, 4, 256, 256, False),       # groups of 256, ragged last group
+    ("q_proj", 318, 40, 2560, 4096, 4, 1024, 1024, False),     # groups of 1024 over four internal blocks
+    ("up_proj", 319, 96, 768, 4096, 4, 32, 128, True, 0.005),  # 4-bit, groups of 32, act-order, damp 0.005
+    ("down_proj", 320, 64, 1536, 4096, 4, 256, 512, True),     # groups of 256 in blocks of 512, act-order
 ]
 
 
@@ -220,10 +225,12 @@ def run_layer(wl, bits, g, B, act, check=True):
     return out, res
 
 
-@pytest.mark.parametrize("name,tag,d_out,d_in,n,bits,g,B,act", LAYER_CASES)
-def test_quantize_layer_parity(name, tag, d_out, d_in, n, bits, g, B, act):
-    wl = synth.WORKLOADS[name].with_shape(tag, d_out, d_in, n)
-    say(f"layer {name} tag={tag} {d_out}x{d_in} n={n} bits={bits} g={g} B={B} act={act}")
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: f"{c[0]}-{c[1]}")
+def test_quantize_layer_parity(case):
+    name, tag, d_out, d_in, n, bits, g, B, act = case[:9]
+    damp = case[9] if len(case) > 9 else synth.WORKLOADS[name].damp
+    wl = synth.WORKLOADS[name].with_shape(tag, d_out, d_in, n, damp=damp)
+    say(f"layer {name} tag={tag} {d_out}x{d_in} n={n} bits={bits} g={g} B={B} act={act} damp={damp}")
     _, res = run_layer(wl, bits, g, B, act)
     say(f"  exempt {res.get('exempt_codes')}+{res.get('exempt_zeros')} mism {res.get('mismatch_codes')}"
         f"+{res.get('mismatch_zeros')} scale {res.get('scale_max_rel')} loss {res.get('loss_rel')} {res.get('worst')}")
@@ -284,11 +291,46 @@ def test_identity_hessian_gives_rtn_on_gpu():
 # full-size layers in the benchmark's configuration (≈ 30-60 s each, most of
 # it the fp64 oracle Hessian on the host)
 # ---------------------------------------------------------------------------
+def one_row_per_group(d_out, seed):
+    """One row from every 16-row work group of the in-block kernel (a seeded
+    pick inside each group), so that every group's output is checked."""
+    rng = np.random.default_rng(seed)
+    return np.array([min(r0 + int(rng.integers(16)), d_out - 1) for r0 in range(0, d_out, 16)])
+
+
+def replay_rows(name, wl, W, X, q, rows, n_chunks):
+    say(f"  oracle Hessian over {X.shape[0]} tokens")
+    H = None
+    for ci, chunk in enumerate(np.array_split(X, n_chunks)):
+        Hc = O.hessian([chunk], wl.dtype, wl.d_in)   # chunk sums add up (pinned)
+        H = Hc if H is None else H + Hc
+        say(f"    chunk {ci + 1}/{n_chunks}")
+    W0 = O.widen(W[rows], wl.dtype)
+    qp = q.qpacked.cpu().numpy().view(np.uint32)[:, rows]
+    sc = q.scales.cpu().numpy()[:, rows]
+    zr = q.zeros.cpu().numpy()[:, rows]
+    perm = q.perm.cpu().numpy()
+    say("  oracle factor (reversed-order route)")
+    Hd = H[np.ix_(perm, perm)]
+    Hd[np.diag_indices(wl.d_in)] += O.damping(H, wl.damp)
+    U = O.inverse_cholesky_upper_reverse(Hd)     # equal to the plain route (pinned)
+    del Hd
+    say(f"  oracle loop on {len(rows)} rows")
+    res = C.check_layer(W0, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order, qp, sc, zr,
+                        perm, U=U)
+    say(f"  {name}: exempt {res.get('exempt_codes')}+{res.get('exempt_zeros')}, mismatches "
+        f"{res.get('mismatch_codes')}+{res.get('mismatch_zeros')}, scale rel {res.get('scale_max_rel'):.2e}, "
+        f"loss rel {res.get('loss_rel'):.2e}, closest oracle t to a boundary {res.get('min_boundary_dist'):.2e} "
+        f"({res.get('within_1e-3_of_boundary')} within 1e-3)")
+    return res
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("name,rows", [("q_proj", 96), ("up_proj", 96), ("down_proj", 64)])
-def test_full_layer_sampled_rows(name, rows):
+@pytest.mark.parametrize("name,rows", [("q_proj", "all"), ("up_proj", "group"), ("down_proj", "group")])
+def test_full_layer_rows(name, rows):
     """Whole layer on the GPU in the benchmark's configuration; the oracle
-    replays a sample of rows (rows are independent given H)."""
+    replays every row (q_proj) or one row of every 16-row work group (rows
+    are independent given H)."""
     wl = synth.WORKLOADS[name]
     say(f"full layer {name}: generating inputs")
     W, X = make(wl)
@@ -296,20 +338,29 @@ def test_full_layer_sampled_rows(name, rows):
     q = P.quantize_layer(to_dev(W, wl.dtype), Hg, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order)
     torch.cuda.synchronize()
     del Hg
-    say("  oracle Hessian")
-    H = None
-    for ci, chunk in enumerate(np.array_split(X, 32)):
-        Hc = O.hessian([chunk], wl.dtype, wl.d_in)   # chunk sums add up (pinned)
-        H = Hc if H is None else H + Hc
-        say(f"    chunk {ci + 1}/32")
-    del X
-    sel = np.sort(np.random.default_rng(1).choice(wl.d_out, rows, replace=False))
-    W0 = O.widen(W[sel], wl.dtype)
-    qp = q.qpacked.cpu().numpy().view(np.uint32)[:, sel]
-    sc = q.scales.cpu().numpy()[:, sel]
-    zr = q.zeros.cpu().numpy()[:, sel]
-    say("  oracle loop")
-    res = C.check_layer(W0, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order, qp, sc, zr,
-                        q.perm.cpu().numpy())
-    say(f"  {res}")
+    sel = np.arange(wl.d_out) if rows == "all" else one_row_per_group(wl.d_out, 1)
+    res = replay_rows(name, wl, W, X, q, sel, 32)
+    assert res["ok"], res
+
+
+@pytest.mark.slow
+def test_full_layer_down70b_rows():
+    """The 70B down_proj shape (8192 x 28672, 4-bit, groups of 128, blocks of
+    256, act-order off) end to end on the GPU: Hessian at d_in = 28672, the
+    batched factorization, 1024-column far batches and the register-staged
+    near update over up to 768 pending columns.  The calibration set is cut
+    to 16384 tokens (two chunks of the same law) so that the oracle's float64
+    Hessian and factor fit the test's time; H then has rank 16384 and the
+    damping carries the rest.  One row of every 16-row work group is
+    replayed."""
+    wl = synth.WORKLOADS["down70b"].with_shape(5, 8192, 28672, 16384)
+    say("down70b layer: generating inputs")
+    W, X = make(wl)
+    Hg = gpu_hessian(X, wl.dtype)
+    say("  GPU quantize_layer")
+    q = P.quantize_layer(to_dev(W, wl.dtype), Hg, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order)
+    torch.cuda.synchronize()
+    del Hg
+    torch.cuda.empty_cache()
+    res = replay_rows("down70b", wl, W, X, q, one_row_per_group(wl.d_out, 2), 2)
     assert res["ok"], res
