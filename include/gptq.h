@@ -21,7 +21,8 @@
  *     stated otherwise.  The caller keeps every buffer alive until the stream
  *     has passed the call.
  *   - The caller owns all memory.  The library never allocates or frees
- *     device memory.
+ *     device memory; the one exception is the fixed static scratch that
+ *     gptq_hessian_accumulate_noalloc keeps per GPU (see there).
  *   - Arguments are validated on the host before anything is enqueued.  On
  *     GPTQ_EINVAL nothing was launched and no output was written;
  *     gptq_last_error() gives a detail string (thread-local).
@@ -83,6 +84,25 @@ GPTQ_API size_t gptq_hessian_workspace_size(int64_t n, int64_t d_in, gptq_dtype 
 GPTQ_API gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, int64_t n, int64_t d_in,
                                     float *H, void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 1 without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same operation, arguments and results as
+ * gptq_hessian_accumulate (equal up to fp32 summation order: the token split
+ * is chosen to fit the scratch), but the partial tiles live in a scratch
+ * array that the library holds statically: 256 MiB per GPU it runs on, kept
+ * until the process ends.  Calls nothing that allocates.  Every call on one
+ * GPU shares that GPU's scratch, so calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialized by the caller.
+ * EINVAL (before anything is enqueued) when the partial tiles do not fit:
+ * d_in above gptq_hessian_noalloc_max_d_in(x_dtype), or at large d_in a token
+ * range long enough to need several token splits (32-bit row offsets limit a
+ * split to 2^30 / d_in tokens); other errors as gptq_hessian_accumulate.
+ * ------------------------------------------------------------------------- */
+GPTQ_API gptq_status gptq_hessian_accumulate_noalloc(const void *X, gptq_dtype x_dtype, int64_t n, int64_t d_in,
+                                                     float *H, void *stream);
+GPTQ_API int64_t gptq_hessian_noalloc_max_d_in(gptq_dtype x_dtype);   /* host only; -1 for a bad dtype */
 
 /* ---------------------------------------------------------------------------
  * Stages 2-5: quantize one layer.

@@ -24,7 +24,8 @@ from dataclasses import dataclass
 __all__ = [
     "GptqError", "lib", "hessian_accumulate", "hessian_workspace_size", "quantize_layer",
     "quantize_layer_workspace_size", "inverse_factor", "packed_words", "num_groups", "QuantizedLayer",
-    "LIB_PATH", "F32", "BF16", "profile_enable", "profile_read",
+    "LIB_PATH", "F32", "BF16", "profile_enable", "profile_read", "hessian_accumulate_noalloc",
+    "hessian_noalloc_max_d_in",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
@@ -51,6 +52,11 @@ def _load() -> ctypes.CDLL:
     L.gptq_hessian_accumulate.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_void_p,
                                           c.c_void_p, c.c_size_t, c.c_void_p]
     L.gptq_hessian_accumulate.restype = c.c_int
+    L.gptq_hessian_accumulate_noalloc.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_void_p,
+                                                  c.c_void_p]
+    L.gptq_hessian_accumulate_noalloc.restype = c.c_int
+    L.gptq_hessian_noalloc_max_d_in.argtypes = [c.c_int]
+    L.gptq_hessian_noalloc_max_d_in.restype = c.c_int64
     L.gptq_quantize_layer_workspace_size.argtypes = [c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int]
     L.gptq_quantize_layer_workspace_size.restype = c.c_size_t
     L.gptq_quantize_layer.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_void_p, c.c_int, c.c_int,
@@ -192,6 +198,24 @@ def hessian_accumulate(X, H, workspace=None, stream=None) -> None:
     _check(_lib().gptq_hessian_accumulate(X.data_ptr() if n else None, code, n, d, H.data_ptr(),
                                        ws.data_ptr() if ws is not None else None,
                                        0 if ws is None else ws.numel(), _stream_ptr(stream)))
+
+
+def hessian_accumulate_noalloc(X, H, stream=None) -> None:
+    """H += 2 X^T X with the library's static scratch instead of a workspace
+    (gptq_hessian_accumulate_noalloc: nothing is allocated; calls that overlap
+    on one GPU race)."""
+    torch = _torch()
+    _require(X, "X", ndim=2)
+    _require(H, "H", dtype=torch.float32, ndim=2)
+    n, d = X.shape
+    if H.shape != (d, d):
+        raise ValueError(f"H must be [{d}, {d}]")
+    _check(_lib().gptq_hessian_accumulate_noalloc(X.data_ptr() if n else None, _dtype_code(X), n, d, H.data_ptr(),
+                                                  _stream_ptr(stream)))
+
+
+def hessian_noalloc_max_d_in(dtype_code: int) -> int:
+    return int(_lib().gptq_hessian_noalloc_max_d_in(dtype_code))
 
 
 def quantize_layer_workspace_size(d_out, d_in, bits, group_size, block_size, act_order) -> int:

@@ -297,6 +297,47 @@ gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, int64_t n
     return GPTQ_OK;
 }
 
+int64_t gptq_hessian_noalloc_max_d_in(gptq_dtype x_dtype) {
+    if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16) return -1;
+    // the largest d_in whose lower tiles fit the scratch with one token split
+    const gptq::HessPlan p1 = gptq::hessian_plan(1, 1, x_dtype == GPTQ_BF16);
+    const int64_t max_slots = (int64_t)(gptq::HESS_STATIC_SCRATCH_BYTES / ((size_t)p1.tile * p1.tile * sizeof(float)));
+    int64_t nb = 0;
+    while ((nb + 1) * (nb + 2) / 2 <= max_slots) ++nb;
+    return nb * p1.tile;
+}
+
+gptq_status gptq_hessian_accumulate_noalloc(const void *X, gptq_dtype x_dtype, int64_t n, int64_t d_in, float *H,
+                                            void *stream) {
+    g_err.clear();
+    if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "x_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (n < 0) return fail(GPTQ_EINVAL, "n must be >= 0");
+    if (d_in < 1 || d_in > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d_in must be in [1, 2^20]");
+    if (!H) return fail(GPTQ_EINVAL, "H is NULL");
+    if (n == 0) return GPTQ_OK;
+    if (!X) return fail(GPTQ_EINVAL, "X is NULL");
+    const int bf = x_dtype == GPTQ_BF16;
+    const gptq::HessPlan p1 = gptq::hessian_plan(1, 1, bf);
+    const int64_t max_slots = (int64_t)(gptq::HESS_STATIC_SCRATCH_BYTES / ((size_t)p1.tile * p1.tile * sizeof(float)));
+    const gptq::HessPlan p = gptq::hessian_plan(n, d_in, bf, max_slots);
+    if (p.slots > max_slots || gptq::hessian_ws_bytes(p) > gptq::HESS_STATIC_SCRATCH_BYTES)
+        return fail(GPTQ_EINVAL, "d_in = %lld needs %lld partial tiles; the static scratch of %zu MiB holds %lld "
+                    "(d_in <= %lld)", (long long)d_in, (long long)p.slots, gptq::HESS_STATIC_SCRATCH_BYTES >> 20,
+                    (long long)max_slots, (long long)gptq_hessian_noalloc_max_d_in(x_dtype));
+    void *scratch = nullptr;
+    HIPCHECK(gptq::hessian_static_scratch(&scratch));
+    hipStream_t st = (hipStream_t)stream;
+    {
+        StageTimer t(0, st);
+        HIPCHECK(gptq::hessian_product_launch(X, bf, n, d_in, (float *)scratch, p, st));
+    }
+    {
+        StageTimer t(1, st);
+        HIPCHECK(gptq::hessian_reduce_launch(d_in, H, (const float *)scratch, p, st));
+    }
+    return GPTQ_OK;
+}
+
 size_t gptq_quantize_layer_workspace_size(int64_t d_out, int64_t d_in, int bits, int group_size, int block_size,
                                           int act_order) {
     (void)act_order;

@@ -29,8 +29,15 @@ struct HessPlan {
     int nwg;           // work groups of the product kernel
     int64_t slots;     // partial tiles written (= nwg)
 };
-HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16);
+// max_slots caps the partial tiles (the token split is chosen within it);
+// the returned plan may still exceed it when even one split does not fit.
+HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16, int64_t max_slots = INT64_MAX);
 size_t hessian_ws_bytes(const HessPlan &p);
+// The library's own scratch for the allocation-free entry point: a static
+// device array of HESS_STATIC_SCRATCH_BYTES per GPU; *ptr = its device
+// address on the current device (resolved on first use, then cached).
+constexpr size_t HESS_STATIC_SCRATCH_BYTES = (size_t)256 << 20;
+hipError_t hessian_static_scratch(void **ptr);
 // product kernel: lower tiles of X^T X per token split -> partial slots
 hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t d, float *partials,
                                   const HessPlan &p, hipStream_t st);

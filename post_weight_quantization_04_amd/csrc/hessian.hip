@@ -22,6 +22,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 namespace gptq {
@@ -597,7 +598,7 @@ int cu_count() {
 
 }  // namespace
 
-HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16) {
+HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16, int64_t max_slots) {
     HessPlan p{};
     p.tile = is_bf16 ? BT : FT;
     const int bk = is_bf16 ? BBK : FBK;
@@ -618,7 +619,7 @@ HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16) {
     for (int s = 1; s <= std::max(smax, 1); ++s) {
         const int64_t nwg = (int64_t)s * p.ntiles;
         const int64_t tok = cdiv(cdiv(std::max<int64_t>(n, 1), s), bk) * bk;
-        if (tok > tok_limit) continue;
+        if (tok > tok_limit || nwg > max_slots) continue;
         const double rounds = (double)cdiv(nwg, cus);
         const double bytes = 2.0 * (double)nwg * p.tile * p.tile * 4.0;
         const double t = rounds * tok * t_tok + bytes / bw;
@@ -639,6 +640,37 @@ HessPlan hessian_plan(int64_t n, int64_t d, int is_bf16) {
 
 size_t hessian_ws_bytes(const HessPlan &p) {
     return align256((size_t)p.slots * p.tile * p.tile * sizeof(float));
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for callers that cannot allocate.  Every GPU that
+// runs the library holds one copy of this array until the process ends; its
+// device address is resolved once per device (with that device current) and
+// kept, because in host code the array's name is only a host-side stand-in.
+// Calls that overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+namespace {
+__device__ __attribute__((aligned(256))) unsigned char scratch[HESS_STATIC_SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t hessian_static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t hessian_product_launch(const void *X, int is_bf16, int64_t n, int64_t d, float *partials,

@@ -116,3 +116,22 @@ def test_inverse_factor_rejects_bad_arguments():
     assert L.gptq_inverse_factor(FAKE, 0, 0.01, 0, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert L.gptq_inverse_factor(FAKE, 10, float("inf"), 0, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert L.gptq_inverse_factor(FAKE, 10, 0.01, 0, FAKE, FAKE, FAKE, 4, None) == 4
+
+
+def test_hessian_noalloc_limits_and_rejections():
+    L = P.lib
+    # the static scratch holds 1024 partial 256x256 tiles (bf16) or 4096 of
+    # 128x128 (fp32): one token split of every lower tile up to these d_in
+    assert P.hessian_noalloc_max_d_in(P.BF16) == 44 * 256
+    assert P.hessian_noalloc_max_d_in(P.F32) == 90 * 128
+    assert P.hessian_noalloc_max_d_in(7) == -1
+    big = P.hessian_noalloc_max_d_in(P.BF16) + 1
+    assert L.gptq_hessian_accumulate_noalloc(FAKE, P.BF16, 100, big, FAKE, None) == 1
+    assert b"static scratch" in L.gptq_last_error()
+    assert L.gptq_hessian_accumulate_noalloc(FAKE, 5, 10, 10, FAKE, None) == 1
+    assert L.gptq_hessian_accumulate_noalloc(FAKE, P.BF16, -1, 10, FAKE, None) == 1
+    assert L.gptq_hessian_accumulate_noalloc(FAKE, P.BF16, 10, 0, FAKE, None) == 1
+    assert L.gptq_hessian_accumulate_noalloc(FAKE, P.BF16, 10, 10, None, None) == 1
+    assert L.gptq_hessian_accumulate_noalloc(None, P.BF16, 10, 10, FAKE, None) == 1
+    # n == 0 is a no-op that touches nothing
+    assert L.gptq_hessian_accumulate_noalloc(None, P.BF16, 0, 10, FAKE, None) == 0
