@@ -74,6 +74,64 @@ def measured_traffic(wl):
     return c.get("hbm_bytes_per_launch")
 
 
+def batch_ends(wl):
+    """Column where each batch of blocks ends (a far update follows every one
+    but the last): batches of eight blocks up to 128 columns wide, of 1024
+    columns for wider ones, cut after a block that ends a group wider than a
+    block; blocks wider than 256 columns run as the widest width <= 256 that
+    keeps every group start on a block start."""
+    d, B = wl.d_in, min(wl.block_size, wl.d_in)
+    g = wl.d_in if (wl.group_size == -1 or wl.group_size >= d) else wl.group_size
+    if B > 256:
+        B = 256 if g >= d else ((256 // g) * g if g <= 256 else next(c for c in range(256, 0, -16) if g % c == 0))
+    far = 8 if B <= 128 else max(1, 1024 // B)
+    ends, e = [], 0
+    while e < d:
+        nblk = 0
+        while nblk < far and e < d:
+            e = min(e + B, d)
+            nblk += 1
+            if g > B and e % g == 0:
+                break
+        ends.append(e)
+    return B, ends
+
+
+def layer_roofline(wl, stages, ms_layer):
+    """Every stage at its own roofline (max of flops at the MFMA peak of its
+    type and bytes at HBM bandwidth), summed, against the measured layer."""
+    d, do, n = wl.d_in, wl.d_out, wl.n
+    xb = 2 if wl.dtype == "bf16" else 4
+    f_h, f_upd = workload_flops(wl)
+    groups = -(-d // (d if (wl.group_size == -1 or wl.group_size >= d) else wl.group_size))
+    words = -(-wl.bits * d // 32)
+    peak_h = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    _, ends = batch_ends(wl)
+    starts = [0] + ends[:-1]
+    f_far = sum(2 * do * (e - p) * (d - e) for p, e in zip(starts, ends) if e < d)
+    work = {   # stage: (flops, flop peak TFLOP/s, bytes)
+        "hessian": (f_h, peak_h, xb * n * d + 8 * d * d),
+        "prep": (0, PEAK_FP32_TFLOPS, 8 * d * d + (xb + 4) * do * d),
+        "factor": (2 * d ** 3 / 3, PEAK_FP32_TFLOPS, 8 * d * d),
+        "update": (f_upd, PEAK_FP32_TFLOPS, 9 * do * d),
+        "pack": (0, PEAK_FP32_TFLOPS, do * d + 4 * words * do + 8 * groups * do),
+    }
+    at_peak = {k: max(f / (p * 1e12), b / (PEAK_HBM_GBS * 1e9)) * 1e3 for k, (f, p, b) in work.items()}
+    ms = lambda k: stages.get(k, {}).get("ms_per_step", 0.0)
+    t_upd = ms("quant_block") + ms("trail_update")
+    rates = {
+        "hessian_product_tflops": f_h / (ms("hessian_product") * 1e9) if ms("hessian_product") else None,
+        "factor_tflops": (2 * d ** 3 / 3) / (ms("factor") * 1e9) if ms("factor") else None,
+        "update_tflops": f_upd / (t_upd * 1e9) if t_upd else None,
+        "trail_update_tflops": f_far / (ms("trail_update") * 1e9) if ms("trail_update") else None,
+        "quant_block_gbs": 9 * do * d / (ms("quant_block") * 1e6) if ms("quant_block") else None,
+        "pack_gbs": (do * d + 4 * words * do) / (ms("pack") * 1e6) if ms("pack") else None,
+    }
+    total = sum(at_peak.values())
+    return {"sum_at_peak_ms": total, "t_layer_ms": ms_layer, "frac": total / ms_layer,
+            "at_peak_ms": at_peak, "trailing_flops": f_far, "stage_rates": rates}
+
+
 def cpu_baseline(wl, W, X):
     """The float64 oracle on a bounded sample of the same workload, scaled to
     the whole layer: Hessian over n_s tokens (scaled by n / n_s), the inverse
@@ -93,15 +151,15 @@ def cpu_baseline(wl, W, X):
         t0 = time.perf_counter()
         H = O.hessian([X[:n_s, :d_s]], wl.dtype, d_s)
         t_h = time.perf_counter() - t0
-        Hd = H + O.damping(H, wl.damp) * np.eye(d_s)
         t0 = time.perf_counter()
-        O.inverse_cholesky_upper(Hd)
+        perm = O.act_order_perm(H) if wl.act_order else np.arange(d_s)
+        Hd = H[np.ix_(perm, perm)] + O.damping(H, wl.damp) * np.eye(d_s)
+        U = O.inverse_cholesky_upper(Hd)
         t_f = time.perf_counter() - t0
         W0 = O.widen(W[:r_s, :d_s], wl.dtype)
         t0 = time.perf_counter()
-        O.gptq(W0, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order)
-        t_g = time.perf_counter() - t0
-    t_loop = max(t_g - t_f, 0.0)
+        O.gptq(W0, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order, perm=perm, U=U)
+        t_loop = time.perf_counter() - t0
     sc = wl.d_in / d_s
     t_full = t_h * (wl.n / n_s) * sc * sc + t_f * sc ** 3 + t_loop * (wl.d_out / r_s) * sc * sc
     f_h, f_upd = workload_flops(wl)
@@ -236,6 +294,7 @@ def main():
                    "act_order": wl.act_order, "damp": wl.damp, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "layer_roofline": layer_roofline(wl, stages, ms_step),
         "stages": stages,
         "flops": {"hessian": f_h, "update": f_upd},
     }
