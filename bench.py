@@ -132,6 +132,42 @@ def layer_roofline(wl, stages, ms_layer):
             "at_peak_ms": at_peak, "trailing_flops": f_far, "stage_rates": rates}
 
 
+def gemv_bench(P, torch, wl, q, Xd, calls=200):
+    """The product with the packed layer just quantized (gptq_dequant_matmul),
+    m = 1 and m = 8 activation rows taken from the calibration set.  The
+    packed weights, scales and zero points are cycled through enough copies
+    (> 256 MB) that the memory-side cache cannot hold them, so every call
+    reads them from HBM; bytes per call = packed words + scales + zero points
+    + activations + outputs."""
+    nbytes_w = q.qpacked.numel() * 4 + (q.scales.numel() + q.zeros.numel()) * 4
+    ncopy = max(2, -(-320 * 2 ** 20 // nbytes_w))
+    copies = [P.QuantizedLayer(q.qpacked.clone(), q.scales.clone(), q.zeros.clone(), q.perm, q.bits, q.group_size,
+                               q.d_in) for _ in range(ncopy)]
+    out = {}
+    stream = torch.cuda.current_stream()
+    for m in (1, 8):
+        A = Xd[:m].contiguous()
+        ws = torch.zeros(max(P.dequant_matmul_workspace_size(m, wl.d_out, wl.d_in, q.bits, q.group_size), 1),
+                         dtype=torch.uint8, device=A.device)
+        Y = [P.dequant_matmul(A, c, workspace=ws) for c in copies[:2]]   # warm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(calls):
+            P.dequant_matmul(A, copies[i % ncopy], workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        nbytes = nbytes_w + A.numel() * A.element_size() + m * wl.d_out * 4
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[f"m{m}"] = {"us_per_call": us, "bytes_per_call": nbytes, "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS,
+                        "frac": gbs / PEAK_HBM_GBS, "weight_copies": ncopy}
+        log(f"bench: dequant product m={m}: {us:.2f} us/call, {gbs:.0f} GB/s")
+    out["bound"] = "hbm"
+    out["layer"] = f"{wl.d_out}x{wl.d_in} {q.bits}-bit group {q.group_size}, the layer just quantized"
+    return out
+
+
 def cpu_baseline(wl, W, X):
     """The float64 oracle on a bounded sample of the same workload, scaled to
     the whole layer: Hessian over n_s tokens (scaled by n / n_s), the inverse
@@ -182,6 +218,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="q_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the product with the packed layer")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -278,6 +315,10 @@ def main():
                 "frac": (achieved / (PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS)) if achieved else None,
                 "traffic": traffic, "avg_launch_ms": avg_h, "algorithmic_flops_per_launch": f_h}
 
+    gemv = None
+    if not args.no_gemv:
+        gemv = gemv_bench(P, torch, wl, step(), Xd)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on a bounded sample")
@@ -295,6 +336,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "layer_roofline": layer_roofline(wl, stages, ms_step),
+        "dequant_gemv": gemv,
         "stages": stages,
         "flops": {"hessian": f_h, "update": f_upd},
     }

@@ -163,6 +163,46 @@ GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float dam
                                 void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Products with a quantized layer: what inference runs on the packed weights.
+ * "Optimization Gptq", "Backends de kernel" (kernels computing with the 4-bit
+ * weights) and "GPTQ (GPT Quantization)", "Limitations" (the weights are
+ * dequantized for each product).
+ *
+ * Y[i][r] = sum_c A[i][c] * W_hat[r][c] for i < m, r < d_out, where
+ * W_hat[r][perm[k]] = scales[k/g][r] * (code(r, k) - zeros[k/g][r]) is the
+ * layer exactly as gptq_quantize_layer stored it (g the effective group size).
+ *   A        device, [m][d_in], a_dtype BF16 or F32, original column order
+ *            (the kernels gather it into processing order through perm).
+ *   Qpacked, scales, zeros, perm
+ *            device, gptq_quantize_layer's outputs for a d_out x d_in layer
+ *            quantized with `bits` and `group_size`.  perm may be NULL
+ *            (identity, as act_order = 0 writes it).
+ *   Y        device, [m][d_out], y_dtype F32 or BF16 (rounded to nearest
+ *            even from the fp32 result).
+ * Codes are multiplied in fp32 with the fp32-widened activations; every 16
+ * codes the group's scale and zero point are applied as
+ * s * (sum A q) - s z * (sum A), and the partial sums of the k-ranges are
+ * added in a fixed order (deterministic).  Up to 8 rows of A per launch (the
+ * decode shape, bound by reading the packed weights); larger m runs in
+ * chunks of 8.
+ * workspace  device scratch of gptq_dequant_matmul_workspace_size(m, d_out,
+ *            d_in, bits, group_size) bytes (0 when m == 0; may then be NULL).
+ *            It holds the k-ranges' partial sums and one completion counter
+ *            per 256 output rows: it must be ZEROED before its first use;
+ *            every call leaves it ready for the next (counters back at zero).
+ *            A workspace serves one call at a time.
+ * m == 0 is a no-op.  Errors: EINVAL (bad sizes, bits, group_size or dtype,
+ * NULL pointer; nothing launched), ENOMEM (workspace too small), EHIP.
+ * ------------------------------------------------------------------------- */
+GPTQ_API size_t gptq_dequant_matmul_workspace_size(int64_t m, int64_t d_out, int64_t d_in, int bits,
+                                                   int group_size);
+GPTQ_API gptq_status gptq_dequant_matmul(const void *A, gptq_dtype a_dtype, int64_t m, int64_t d_in,
+                                         const uint32_t *Qpacked, const float *scales, const float *zeros,
+                                         const int32_t *perm, int64_t d_out, int bits, int group_size,
+                                         void *Y, gptq_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
+/* ---------------------------------------------------------------------------
  * Stage timing (tracing aid).  gptq_profile_enable(stage_mask): bit s set
  * makes every later call record a pair of hipEvents around stage s's launches
  * on the caller's stream (GPTQ_PROFILE_ALL: every stage; 0: none).  Reading

@@ -58,7 +58,7 @@ __all__ = [
     "widen", "hessian", "act_order_perm", "damping", "inverse_cholesky_upper",
     "inverse_cholesky_upper_reverse", "group_params", "quantize_values", "gptq",
     "obq_naive", "rtn", "pack", "unpack", "packed_words", "dequantize",
-    "proxy_loss", "n_groups",
+    "proxy_loss", "n_groups", "dequant_matmul",
 ]
 
 
@@ -348,6 +348,21 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, perm: n
     out = np.empty_like(deq)
     out[:, np.asarray(perm)] = deq
     return out
+
+
+def dequant_matmul(A: np.ndarray, qpacked: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                   perm: np.ndarray, bits: int, group_size: int, d_in: int) -> np.ndarray:
+    """Y = A W_hat^T for a packed layer, in float64: unpack the codes,
+    dequantize them into the original column order, multiply.
+
+    The product that inference runs on the quantized weights ("Optimization
+    Gptq", section "Backends de kernel"; "GPTQ (GPT Quantization)",
+    "Limitations": dequantization before each product).  A: [m, d_in]
+    activations in the original column order (float64 values).
+    """
+    codes = unpack(qpacked, bits, d_in)
+    W_hat = dequantize(codes, scales, zeros, perm, _eff_group(d_in, group_size))
+    return np.asarray(A, dtype=np.float64) @ W_hat.T
 
 
 def proxy_loss(W0: np.ndarray, W_hat: np.ndarray, H: np.ndarray) -> float:

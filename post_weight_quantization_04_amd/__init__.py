@@ -25,7 +25,7 @@ __all__ = [
     "GptqError", "lib", "hessian_accumulate", "hessian_workspace_size", "quantize_layer",
     "quantize_layer_workspace_size", "inverse_factor", "packed_words", "num_groups", "QuantizedLayer",
     "LIB_PATH", "F32", "BF16", "profile_enable", "profile_read", "hessian_accumulate_noalloc",
-    "hessian_noalloc_max_d_in",
+    "hessian_noalloc_max_d_in", "dequant_matmul", "dequant_matmul_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
@@ -63,6 +63,12 @@ def _load() -> ctypes.CDLL:
                                       c.c_int, c.c_float, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
                                       c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
     L.gptq_quantize_layer.restype = c.c_int
+    L.gptq_dequant_matmul_workspace_size.argtypes = [c.c_int64, c.c_int64, c.c_int64, c.c_int, c.c_int]
+    L.gptq_dequant_matmul_workspace_size.restype = c.c_size_t
+    L.gptq_dequant_matmul.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p, c.c_void_p,
+                                      c.c_void_p, c.c_int64, c.c_int, c.c_int, c.c_void_p, c.c_int, c.c_void_p,
+                                      c.c_size_t, c.c_void_p]
+    L.gptq_dequant_matmul.restype = c.c_int
     L.gptq_inverse_factor.argtypes = [c.c_void_p, c.c_int64, c.c_float, c.c_int, c.c_void_p, c.c_void_p,
                                       c.c_void_p, c.c_size_t, c.c_void_p]
     L.gptq_inverse_factor.restype = c.c_int
@@ -259,6 +265,37 @@ def quantize_layer(W, H, bits: int = 4, group_size: int = 128, block_size: int =
                                    0 if ws is None else ws.numel(), _stream_ptr(stream)))
     g_eff = d_in if (group_size == -1 or group_size >= d_in) else group_size
     return QuantizedLayer(q, sc, zr, pm, bits, g_eff, d_in)
+
+
+def dequant_matmul_workspace_size(m, d_out, d_in, bits, group_size) -> int:
+    return int(_lib().gptq_dequant_matmul_workspace_size(m, d_out, d_in, bits, group_size))
+
+
+def dequant_matmul(A, q: "QuantizedLayer", out_dtype=None, workspace=None, stream=None, use_perm: bool = True):
+    """Y = A W_hat^T on the packed layer q (gptq_dequant_matmul).  A: [m, d_in]
+    bfloat16/float32 activations in the original column order; returns Y
+    [m, d_out] in out_dtype (float32 by default, or bfloat16).  A workspace
+    passed in must have been zeroed before its first use (calls leave it so)."""
+    torch = _torch()
+    _require(A, "A", ndim=2)
+    m, d_in = A.shape
+    if d_in != q.d_in:
+        raise ValueError(f"A has {d_in} columns, the layer {q.d_in}")
+    d_out = q.scales.shape[1]
+    out_dtype = out_dtype or torch.float32
+    Y = torch.empty((m, d_out), dtype=out_dtype, device=A.device)
+    need = dequant_matmul_workspace_size(m, d_out, d_in, q.bits, q.group_size)
+    # zeroed before its first use (completion counters); calls leave it so
+    if workspace is not None and workspace.numel() * workspace.element_size() >= need:
+        ws = workspace
+    else:
+        ws = torch.zeros(need, dtype=torch.uint8, device=A.device) if need else None
+    _check(_lib().gptq_dequant_matmul(A.data_ptr() if m else None, _dtype_code(A), m, d_in, q.qpacked.data_ptr(),
+                                      q.scales.data_ptr(), q.zeros.data_ptr(),
+                                      q.perm.data_ptr() if use_perm else None, d_out, q.bits, q.group_size,
+                                      Y.data_ptr(), _dtype_code(Y), ws.data_ptr() if ws is not None else None,
+                                      0 if ws is None else ws.numel(), _stream_ptr(stream)))
+    return Y
 
 
 def inverse_factor(H, damp: float = 0.01, act_order: bool = False, workspace=None, stream=None):

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgptq.so")
 
-SOURCES = ["api.cpp", "hessian.hip", "prep.hip", "factor.hip", "quant.hip", "trail.hip", "pack.hip"]
+SOURCES = ["api.cpp", "hessian.hip", "prep.hip", "factor.hip", "quant.hip", "trail.hip", "pack.hip", "dequant.hip"]
 ARCH = "gfx950"
 
 

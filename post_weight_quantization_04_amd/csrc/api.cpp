@@ -197,6 +197,21 @@ gptq_status read_pivot_flag(const Workspace &w, hipStream_t st) {
     return GPTQ_OK;
 }
 
+gptq_status check_dequant(int64_t m, int64_t d_out, int64_t d_in, int bits, int group_size, int &g_eff) {
+    if (m < 0) return fail(GPTQ_EINVAL, "m must be >= 0");
+    if (d_out < 1 || d_in < 1) return fail(GPTQ_EINVAL, "d_out and d_in must be >= 1");
+    if (d_in > (int64_t)1 << 30 || d_out > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "dimension too large");
+    if (!valid_bits(bits)) return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+    if (group_size == -1 || group_size >= d_in) {
+        g_eff = (int)d_in;
+    } else {
+        if (group_size < 1 || group_size % 16 != 0)
+            return fail(GPTQ_EINVAL, "group_size must be -1 or a multiple of 16 (got %d)", group_size);
+        g_eff = group_size;
+    }
+    return GPTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,6 +442,50 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
         HIPCHECK(gptq::pack_launch(w.codes, d_out, d_in, bits, Qpacked, st));
     }
     return read_pivot_flag(w, st);
+}
+
+size_t gptq_dequant_matmul_workspace_size(int64_t m, int64_t d_out, int64_t d_in, int bits, int group_size) {
+    int g = 0;
+    if (check_dequant(m, d_out, d_in, bits, group_size, g) != GPTQ_OK) return 0;
+    if (m == 0) return 0;
+    return gptq::dequant_ws_layout(m, d_out, d_in, bits).bytes;
+}
+
+gptq_status gptq_dequant_matmul(const void *A, gptq_dtype a_dtype, int64_t m, int64_t d_in, const uint32_t *Qpacked,
+                                const float *scales, const float *zeros, const int32_t *perm, int64_t d_out,
+                                int bits, int group_size, void *Y, gptq_dtype y_dtype, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    g_err.clear();
+    int g = 0;
+    gptq_status s = check_dequant(m, d_out, d_in, bits, group_size, g);
+    if (s != GPTQ_OK) return s;
+    if (a_dtype != GPTQ_F32 && a_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "a_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (y_dtype != GPTQ_F32 && y_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "y_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (m == 0) return GPTQ_OK;
+    if (!A || !Qpacked || !scales || !zeros || !Y) return fail(GPTQ_EINVAL, "a required pointer is NULL");
+    const gptq::DequantWs wl = gptq::dequant_ws_layout(m, d_out, d_in, bits);
+    const size_t need = wl.bytes;
+    if (!workspace || workspace_bytes < need)
+        return fail(GPTQ_ENOMEM, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    gptq::DequantArgs a{};
+    a.A = A;
+    a.a_bf16 = a_dtype == GPTQ_BF16;
+    a.perm = perm;
+    a.Q = Qpacked;
+    a.scales = scales;
+    a.zeros = zeros;
+    a.Y = Y;
+    a.y_bf16 = y_dtype == GPTQ_BF16;
+    a.part = (float *)workspace;
+    a.counters = (int32_t *)((char *)workspace + wl.counters_off);
+    a.m = m;
+    a.d_in = d_in;
+    a.d_out = d_out;
+    a.bits = bits;
+    a.group = g;
+    a.ngroups = (int)cdiv(d_in, g);
+    HIPCHECK(gptq::dequant_matmul_launch(a, (hipStream_t)stream));
+    return GPTQ_OK;
 }
 
 gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float damp, int act_order, int32_t *perm, float *U,

@@ -127,4 +127,29 @@ hipError_t trail_launch(const QuantArgs &a, int64_t u_row0, int64_t K, int64_t c
 hipError_t pack_launch(const uint8_t *codes, int64_t d_out, int64_t d_in, int bits,
                        uint32_t *Qpacked, hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Products with a packed layer (dequant.hip): Y = A W_hat^T
+// ---------------------------------------------------------------------------
+constexpr int GV_MAX_M = 8;   // activation rows per skinny launch
+struct DequantArgs {
+    const void *A;          // [m][d_in] activations, original column order
+    int a_bf16;             // A is bf16 (else fp32)
+    const int32_t *perm;    // [d_in] processing order, NULL: identity
+    const uint32_t *Q;      // [words][d_out] packed codes
+    const float *scales;    // [G][d_out]
+    const float *zeros;     // [G][d_out]
+    void *Y;                // [m][d_out]
+    int y_bf16;             // Y is bf16 (else fp32)
+    float *part;            // workspace: partial sums of the k-ranges
+    int32_t *counters;      // workspace: one per 256-row tile, zero between calls
+    int64_t m, d_in, d_out;
+    int bits, group;        // group: effective group size
+    int ngroups;
+};
+struct DequantWs {
+    size_t counters_off, counters_bytes, bytes;
+};
+DequantWs dequant_ws_layout(int64_t m, int64_t d_out, int64_t d_in, int bits);
+hipError_t dequant_matmul_launch(const DequantArgs &a, hipStream_t st);
+
 }  // namespace gptq

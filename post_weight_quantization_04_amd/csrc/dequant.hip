@@ -1,0 +1,391 @@
+// Products with a GPTQ-packed layer: Y = A W_hat^T, the weights dequantized
+// on the fly.  "Optimization Gptq", "Backends de kernel" (kernels that run
+// the quantized model on its 4-bit weights) and "GPTQ (GPT Quantization)",
+// "Limitations" (weights are dequantized for each product).
+//
+// Storage (as the quantizer writes it): codes in processing order as a
+// little-endian bit stream per row, word-major Qpacked [words][d_out];
+// scales and zeros [groups][d_out]; W_hat[r][perm[k]] = s[k/g][r] (q - z).
+// With A_p[i][k] = A[i][perm[k]] (activations moved into processing order),
+//   Y[i][r] = sum_k A_p[i][k] s[k/g][r] (q[r][k] - z[k/g][r]).
+//
+// Skinny path (m <= 8 activation rows; decode), bound by reading the packed
+// weights once.  A work group owns 256 output rows (four adjacent rows per
+// lane, so a packed word row is one contiguous kilobyte read by a wave as
+// 16-byte loads) and one of `nsplit` ranges of k; k is cut into 32-code units
+// (a unit is `bits` consecutive words of a row) and the group's four waves
+// take every fourth unit of its range.  The group gathers its range of A_p
+// into LDS as fp32, with the sum of every 16 consecutive activations.  Codes
+// are extracted with constant shifts and multiplied with the broadcast
+// activations into a 16-code dot product, folded as
+//   acc += s dot - (s z) sum16(A_p),
+// so the group's scale and zero point are applied once per 16 codes and a
+// group may end at any multiple of 16.  The units' packed words, scales and
+// zero points are loaded a few units ahead, the first ones before the
+// activations are staged.  The four waves' sums meet in LDS; the k-ranges'
+// partial sums go to the workspace, and the last work group of a row tile to
+// finish (a device-scope counter per tile, reset by that group) adds them in
+// split order and writes Y as fp32 or bf16: deterministic, one launch.  No
+// work group ever waits for another.
+#include "common.h"
+
+#include <algorithm>
+
+namespace gptq {
+
+namespace {
+
+constexpr int UNIT = 32;          // codes per unit
+constexpr int GV_ROWS = 256;      // output rows per work group
+constexpr int GV_LDS = 15360;     // staged activations (floats, 60 KB)
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (unsigned)b << 16);
+}
+
+// code k (compile-time, 0..31) of a unit held in BITS words
+template <int BITS, int K>
+__device__ __forceinline__ unsigned unit_code(const unsigned (&w)[BITS]) {
+    constexpr int pos = BITS * K, j = pos >> 5, sh = pos & 31;
+    constexpr unsigned mask = (1u << BITS) - 1u;
+    if constexpr (sh + BITS <= 32) {
+        return __builtin_amdgcn_ubfe(w[j], sh, BITS);
+    } else {
+        return __builtin_amdgcn_alignbit(w[j + 1], w[j], sh) & mask;
+    }
+}
+
+// dot[j][i] += sum over codes 16H .. 16H+15 of the unit of al[i][k] * code_k
+// of row j; each activation is read once and used for the four rows
+template <int BITS, int M, int H, int... KK>
+__device__ __forceinline__ void half_unit_dot(const u32x4 (&w)[BITS], const float *al, int astride,
+                                              float (&dot)[4][M], std::integer_sequence<int, KK...>) {
+    auto one = [&](auto kc) {
+        constexpr int k = decltype(kc)::value + 16 * H;
+        float a[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) a[i] = al[i * astride + k];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            unsigned wj[BITS];
+#pragma unroll
+            for (int b = 0; b < BITS; ++b) wj[b] = w[b][j];
+            const float c = (float)unit_code<BITS, k>(wj);
+#pragma unroll
+            for (int i = 0; i < M; ++i) dot[j][i] = fmaf(a[i], c, dot[j][i]);
+        }
+    };
+    (one(std::integral_constant<int, KK>{}), ...);
+}
+
+// units whose packed words are in flight per lane (about 8 words of registers)
+template <int BITS>
+constexpr int prefetch_units() {
+    return BITS <= 2 ? 4 : (BITS <= 4 ? 2 : 1);
+}
+
+template <int BITS, int M, bool VEC, bool G32>
+__global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A, int a_bf16,
+                                                      const int32_t *__restrict__ perm,
+                                                      const uint32_t *__restrict__ Q,
+                                                      const float *__restrict__ scales,
+                                                      const float *__restrict__ zeros, void *__restrict__ Y,
+                                                      int y_bf16, float *__restrict__ part,
+                                                      int32_t *__restrict__ counters, int64_t m_total, int64_t m0,
+                                                      int64_t d_in, int64_t d_out, int g, int ngroups, int nunits,
+                                                      int nsplit, int64_t nwords) {
+    constexpr int PF = prefetch_units<BITS>();
+    __shared__ __attribute__((aligned(16))) float a_lds[GV_LDS];
+    __shared__ float hs_lds[GV_LDS / 16];
+    __shared__ int last_flag;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int split = blockIdx.y;
+    const int u0 = (int)((int64_t)split * nunits / nsplit), u1 = (int)((int64_t)(split + 1) * nunits / nsplit);
+    const int nu = u1 - u0;                    // M * nu * 32 <= GV_LDS (host plan)
+    const int kw = nu * UNIT;
+    const int64_t r0 = (int64_t)blockIdx.x * GV_ROWS + 4 * lane;
+    bool rv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rv[j] = r0 + j < d_out;
+    const bool any_row = rv[0];
+
+    auto load4 = [&](const uint32_t *base, int64_t off, u32x4 &out) {
+        if (VEC) {   // d_out % 4 == 0: the lane's four rows exist together
+            out = any_row ? *(const u32x4 *)(base + off + r0) : u32x4{0u, 0u, 0u, 0u};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[j] = rv[j] ? base[off + r0 + j] : 0u;
+        }
+    };
+    auto loadf4 = [&](const float *base, int64_t off, f32x4 &out) {
+        if (VEC) {
+            out = any_row ? *(const f32x4 *)(base + off + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[j] = rv[j] ? base[off + r0 + j] : 0.f;
+        }
+    };
+    // a unit's words (zero past the end of the stream), scales and zero
+    // points (G32: both halves of every unit lie in one group)
+    struct Slot {
+        u32x4 w[BITS];
+        f32x4 s[G32 ? 1 : 2], z[G32 ? 1 : 2];
+    };
+    auto fetch = [&](int u, Slot &sl) {
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            const int64_t wi = (int64_t)u * BITS + b;
+            if (wi < nwords)
+                load4(Q, wi * d_out, sl.w[b]);
+            else
+                sl.w[b] = u32x4{0u, 0u, 0u, 0u};
+        }
+        // past d_in (a ragged last unit) the activations are zero; the last
+        // group's parameters stand in for the missing ones
+#pragma unroll
+        for (int h = 0; h < (G32 ? 1 : 2); ++h) {
+            const int64_t gi = std::min<int64_t>(((int64_t)u * UNIT + 16 * h) / g, ngroups - 1);
+            loadf4(scales, gi * d_out, sl.s[h]);
+            loadf4(zeros, gi * d_out, sl.z[h]);
+        }
+    };
+
+    float acc[4][M];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < M; ++i) acc[j][i] = 0.f;
+
+    // this wave's units of the range: wave, wave + 4, ...
+    const int nmy = wave < nu ? (nu - 1 - wave) / 4 + 1 : 0;
+    Slot sl[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < nmy) fetch(u0 + wave + 4 * p, sl[p]);
+    // stage A_p for the range (rows past m_total read 0)
+    const int64_t k0 = (int64_t)u0 * UNIT;
+    for (int idx = tid; idx < M * kw; idx += 256) {
+        const int i = idx / kw, kk = idx - i * kw;
+        const int64_t k = k0 + kk, row = m0 + i;
+        float v = 0.f;
+        if (k < d_in && row < m_total) {
+            const int64_t c = perm ? (int64_t)perm[k] : k;
+            v = a_bf16 ? bf16_bits_to_f32(((const uint16_t *)A)[row * d_in + c]) : ((const float *)A)[row * d_in + c];
+        }
+        a_lds[i * kw + kk] = v;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < M * 2 * nu; idx += 256) {
+        const int i = idx / (2 * nu), h = idx - i * 2 * nu;
+        const float *p = a_lds + i * kw + 16 * h;
+        float s = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s += p[t];
+        hs_lds[i * 2 * nu + h] = s;
+    }
+    __syncthreads();
+    for (int i0 = 0; i0 < nmy; i0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int it = i0 + p;
+            if (it < nmy) {
+                const int ul = wave + 4 * it;          // unit within the range
+                const float *al = a_lds + ul * UNIT;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float hs[M];
+#pragma unroll
+                    for (int i = 0; i < M; ++i) hs[i] = hs_lds[i * 2 * nu + 2 * ul + h];
+                    float dot[4][M];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int i = 0; i < M; ++i) dot[j][i] = 0.f;
+                    if (h == 0)
+                        half_unit_dot<BITS, M, 0>(sl[p].w, al, kw, dot, std::make_integer_sequence<int, 16>{});
+                    else
+                        half_unit_dot<BITS, M, 1>(sl[p].w, al, kw, dot, std::make_integer_sequence<int, 16>{});
+                    const int hh = G32 ? 0 : h;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float sj = sl[p].s[hh][j], szj = sj * sl[p].z[hh][j];
+#pragma unroll
+                        for (int i = 0; i < M; ++i) acc[j][i] = fmaf(sj, dot[j][i], fmaf(-szj, hs[i], acc[j][i]));
+                    }
+                }
+                if (it + PF < nmy) fetch(u0 + wave + 4 * (it + PF), sl[p]);
+            }
+        }
+    }
+
+    // the four waves' sums, added in wave order: red[wave][row][i]
+    __syncthreads();
+    float *red = a_lds;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < M; ++i) red[(wave * GV_ROWS + 4 * lane + j) * M + i] = acc[j][i];
+    __syncthreads();
+    // thread t: row t of the tile, all M activation rows
+    const int64_t r = (int64_t)blockIdx.x * GV_ROWS + tid;
+    float mine[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v += red[(w * GV_ROWS + tid) * M + i];
+        mine[i] = v;
+    }
+    auto store_y = [&](int i, float v) {
+        const int64_t o = (m0 + i) * d_out + r;
+        if (y_bf16) {
+            const unsigned u = __builtin_bit_cast(unsigned, v);   // round to nearest even
+            ((uint16_t *)Y)[o] = (uint16_t)((u + ((u >> 16) & 1u) + 0x7FFFu) >> 16);
+        } else {
+            ((float *)Y)[o] = v;
+        }
+    };
+    if (nsplit == 1) {
+        if (r < d_out)
+#pragma unroll
+            for (int i = 0; i < M; ++i)
+                if (m0 + i < m_total) store_y(i, mine[i]);
+        return;
+    }
+    // Partial sums of this k-range, then the tile's last group adds them all.
+    // The partials are device-scope atomic stores and loads (written through
+    // to, and read from, the point where all XCDs see memory alike, past the
+    // per-XCD L2), and every store has completed (vmcnt drained) before this
+    // group's count is added; the group that adds the last count therefore
+    // reads every partial.  This is the ordering a device-scope release and
+    // acquire give, without writing back and invalidating the whole L2 in
+    // every group (which made the product three times slower).
+    if (r < d_out)
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+            __hip_atomic_store(&part[((int64_t)split * M + i) * d_out + r], mine[i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == nsplit - 1;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    if (r < d_out) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            // split order, eight loads in flight at a time
+            float v = 0.f;
+            for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+                float t[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int sp = sp0 + q;
+                    t[q] = (sp >= nsplit) ? 0.f
+                         : (sp == split ? mine[i]
+                                        : __hip_atomic_load(&part[((int64_t)sp * M + i) * d_out + r],
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (sp0 + q < nsplit) v += t[q];
+            }
+            if (m0 + i < m_total) store_y(i, v);
+        }
+    }
+    if (tid == 0) counters[blockIdx.x] = 0;    // ready for the next call on this workspace
+}
+
+// work groups along k for a launch of M activation rows: about 128 work
+// groups in all for layers under 16 MB of packed words (fixed costs per group
+// dominate there) and 512 above, each wave with at least one unit, the staged
+// range within LDS (measured on q_proj, up_proj and the 70B down_proj)
+int gemv_splits(int M, int64_t d_out, int64_t d_in, int bits) {
+    const int nunits = (int)cdiv(d_in, UNIT);
+    const int64_t tiles = cdiv(d_out, GV_ROWS);
+    const int max_units = GV_LDS / (M * UNIT);
+    const int64_t packed = d_out * cdiv((int64_t)bits * d_in, 32) * 4;
+    const int64_t target = packed < ((int64_t)16 << 20) ? 128 : 512;
+    int64_t s = std::max<int64_t>(1, target / tiles);
+    s = std::min<int64_t>(s, std::max(1, nunits / 4));
+    s = std::max<int64_t>(s, cdiv(nunits, max_units));
+    return (int)s;
+}
+
+int pad_m(int64_t mc) { return mc <= 1 ? 1 : (mc <= 2 ? 2 : (mc <= 4 ? 4 : 8)); }
+
+template <int BITS, int M, bool VEC, bool G32>
+void launch_gemv_k(const DequantArgs &a, int64_t m0, hipStream_t st) {
+    const int nsplit = gemv_splits(M, a.d_out, a.d_in, BITS);
+    const dim3 grid((unsigned)cdiv(a.d_out, GV_ROWS), (unsigned)nsplit);
+    const int nunits = (int)cdiv(a.d_in, UNIT);
+    const int64_t nwords = cdiv((int64_t)BITS * a.d_in, 32);
+    dq_gemv_kernel<BITS, M, VEC, G32><<<grid, 256, 0, st>>>(a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y,
+                                                            a.y_bf16, a.part, a.counters, a.m, m0, a.d_in, a.d_out,
+                                                            a.group, a.ngroups, nunits, nsplit, nwords);
+}
+
+template <int BITS, int M>
+hipError_t launch_gemv_m(const DequantArgs &a, int64_t m0, hipStream_t st) {
+    const bool vec = a.d_out % 4 == 0;
+    const bool g32 = a.group % 32 == 0 || a.ngroups == 1;
+    if (vec && g32)
+        launch_gemv_k<BITS, M, true, true>(a, m0, st);
+    else if (vec)
+        launch_gemv_k<BITS, M, true, false>(a, m0, st);
+    else if (g32)
+        launch_gemv_k<BITS, M, false, true>(a, m0, st);
+    else
+        launch_gemv_k<BITS, M, false, false>(a, m0, st);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_gemv_bits(const DequantArgs &a, hipStream_t st) {
+    for (int64_t m0 = 0; m0 < a.m; m0 += GV_MAX_M) {
+        const int M = pad_m(std::min<int64_t>(GV_MAX_M, a.m - m0));
+        hipError_t e;
+        if (M == 1)
+            e = launch_gemv_m<BITS, 1>(a, m0, st);
+        else if (M == 2)
+            e = launch_gemv_m<BITS, 2>(a, m0, st);
+        else if (M == 4)
+            e = launch_gemv_m<BITS, 4>(a, m0, st);
+        else
+            e = launch_gemv_m<BITS, 8>(a, m0, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+// Workspace: the partial sums of the widest launch ([nsplit][M][d_out] fp32),
+// then one counter per row tile (zero between calls).
+DequantWs dequant_ws_layout(int64_t m, int64_t d_out, int64_t d_in, int bits) {
+    DequantWs w{};
+    size_t part = 0;
+    for (int64_t m0 = 0; m0 < m; m0 += GV_MAX_M) {
+        const int M = pad_m(std::min<int64_t>(GV_MAX_M, m - m0));
+        const int s = gemv_splits(M, d_out, d_in, bits);
+        if (s > 1) part = std::max(part, (size_t)s * M * d_out * sizeof(float));
+    }
+    w.counters_off = align256(part);
+    w.counters_bytes = (size_t)cdiv(d_out, GV_ROWS) * sizeof(int32_t);
+    w.bytes = m > 0 ? align256(w.counters_off + w.counters_bytes) : 0;
+    return w;
+}
+
+hipError_t dequant_matmul_launch(const DequantArgs &a, hipStream_t st) {
+    switch (a.bits) {
+        case 2: return launch_gemv_bits<2>(a, st);
+        case 3: return launch_gemv_bits<3>(a, st);
+        case 4: return launch_gemv_bits<4>(a, st);
+        case 8: return launch_gemv_bits<8>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gptq

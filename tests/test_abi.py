@@ -135,3 +135,27 @@ def test_hessian_noalloc_limits_and_rejections():
     assert L.gptq_hessian_accumulate_noalloc(None, P.BF16, 10, 10, FAKE, None) == 1
     # n == 0 is a no-op that touches nothing
     assert L.gptq_hessian_accumulate_noalloc(None, P.BF16, 0, 10, FAKE, None) == 0
+
+
+def test_dequant_matmul_rejects_bad_arguments():
+    L = P.lib
+    ok = dict(A=FAKE, at=P.BF16, m=2, d_in=256, Q=FAKE, S=FAKE, Z=FAKE, perm=None, d_out=64, bits=4, g=128,
+              Y=FAKE, yt=P.F32, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.gptq_dequant_matmul(a["A"], a["at"], a["m"], a["d_in"], a["Q"], a["S"], a["Z"], a["perm"],
+                                     a["d_out"], a["bits"], a["g"], a["Y"], a["yt"], a["ws"], a["wsb"], None)
+
+    for kw in (dict(A=None), dict(Q=None), dict(S=None), dict(Z=None), dict(Y=None), dict(m=-1), dict(d_in=0),
+               dict(d_out=0), dict(bits=5), dict(g=100), dict(g=0), dict(at=7), dict(yt=7)):
+        assert call(**kw) == 1, kw
+    assert call(m=0, A=None, ws=None, wsb=0) == 0          # no-op
+    # partial sums of the k-ranges (a multiple of one 4096-row fp32 vector),
+    # then 16 tile counters in their own 256-byte block
+    ws = P.dequant_matmul_workspace_size(1, 4096, 4096, 4, 128)
+    assert ws > 4096 * 4 and (ws - 256) % (4096 * 4) == 0
+    assert call(wsb=16) == 4
+    assert P.dequant_matmul_workspace_size(0, 4096, 4096, 4, 128) == 0
+    assert P.dequant_matmul_workspace_size(1, 4096, 4096, 5, 128) == 0

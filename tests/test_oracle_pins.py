@@ -463,3 +463,38 @@ def test_hessian_check_rule():
     Hb = H.copy()
     Hb[3, 5] += 1e-3 * np.sqrt(H[3, 3] * H[5, 5])
     assert not C.check_hessian(Hb, H)["ok"]
+
+
+# --------------------------------------------------------------------------
+# dequantize-then-multiply on a packed layer: hand-worked products
+# (tests/golden/dequant_matmul_examples.json), and the same product built
+# from a quantized layer against the quantizer's own w_hat
+# --------------------------------------------------------------------------
+def test_dequant_matmul_hand_examples():
+    cases = json.load(open(os.path.join(GOLDEN, "dequant_matmul_examples.json")))["cases"]
+    for c in cases:
+        qp = np.array(c["qpacked"], dtype=np.uint32)
+        # the stored words are the hand-derived bit streams of the codes
+        assert [int(v) for v in qp.reshape(-1)] == [int(h, 16) for h in c["qpacked_hex"]], c["name"]
+        assert np.array_equal(O.unpack(qp, c["bits"], c["d_in"]), np.array(c["codes"])), c["name"]
+        g = c["d_in"] if c["group_size"] == -1 else c["group_size"]
+        Wh = O.dequantize(np.array(c["codes"]), c["scales"], c["zeros"], np.array(c["perm"]), g)
+        assert np.array_equal(Wh, np.array(c["W_hat"])), c["name"]
+        Y = O.dequant_matmul(np.array(c["A"], dtype=np.float64), qp, c["scales"], c["zeros"], np.array(c["perm"]),
+                             c["bits"], c["group_size"], c["d_in"])
+        assert np.array_equal(Y, np.array(c["Y"])), c["name"]
+
+
+def test_dequant_matmul_reproduces_quantized_layer():
+    rng = _rng(15)
+    d_in, d_out = 96, 20
+    X, H = _spd_from_x(rng, 300, d_in, scales=np.exp(rng.standard_normal(d_in)))
+    W = rng.standard_normal((d_out, d_in)) * 0.02
+    r = O.gptq(W, H, 3, 32, 32, 0.01, True)
+    qp = O.pack(r["codes"], 3)
+    A = rng.standard_normal((5, d_in))
+    Y = O.dequant_matmul(A, qp, r["scales"], r["zeros"], r["perm"], 3, 32, d_in)
+    # the quantizer's dequantized values, processing order, moved back by perm
+    W_back = np.empty_like(r["w_hat"])
+    W_back[:, r["perm"]] = r["w_hat"]
+    assert np.allclose(Y, A @ W_back.T, rtol=1e-13, atol=1e-15)
