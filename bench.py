@@ -142,7 +142,7 @@ def gemv_bench(P, torch, wl, q, Xd, calls=200):
     nbytes_w = q.qpacked.numel() * 4 + (q.scales.numel() + q.zeros.numel()) * 4
     ncopy = max(2, -(-320 * 2 ** 20 // nbytes_w))
     copies = [P.QuantizedLayer(q.qpacked.clone(), q.scales.clone(), q.zeros.clone(), q.perm, q.bits, q.group_size,
-                               q.d_in) for _ in range(ncopy)]
+                               q.d_in, q.act_order) for _ in range(ncopy)]
     out = {}
     stream = torch.cuda.current_stream()
     for m in (1, 8):
@@ -211,6 +211,90 @@ def cpu_baseline(wl, W, X):
     }
 
 
+def run_block(args, P, synth, torch, np):
+    """One step = every linear layer of one transformer block: per input, H
+    over the calibration tokens, then gptq_quantize_layers on the layers that
+    read that input (one factorization per input instead of per layer)."""
+    groups = synth.block_workloads(args.workload)
+    b = synth.BLOCKS[args.workload]
+    dev = "cuda:0"
+    log(f"bench: generating the {args.workload} inputs ({len(groups)} inputs, "
+        f"{sum(len(l) for _, l in groups)} layers, n={b['n']} tokens)")
+    t0 = time.perf_counter()
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    data = []
+    for xw, lws in groups:
+        Xd = bf(synth.make_x(xw))
+        Wds = [bf(synth.make_w(lw)) for lw in lws]
+        data.append((xw, lws, Xd, Wds))
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
+    dmax = max(xw.d_in for xw, *_ in data)
+    H = torch.zeros(dmax * dmax, dtype=torch.float32, device=dev)
+    ws_h = torch.empty(max(max(P.hessian_workspace_size(b["n"], xw.d_in, P.BF16) for xw, *_ in data), 1),
+                       dtype=torch.uint8, device=dev)
+    import ctypes
+    need = 0
+    for xw, lws, _, _ in data:
+        d_outs = (ctypes.c_int64 * len(lws))(*[lw.d_out for lw in lws])
+        need = max(need, P.lib.gptq_quantize_layers_workspace_size(len(lws), d_outs, xw.d_in, b["bits"],
+                                                                   b["group_size"], b["block_size"],
+                                                                   int(b["act_order"])))
+    ws_q = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step():
+        out = []
+        for xw, lws, Xd, Wds in data:
+            Hg = H[:xw.d_in * xw.d_in].view(xw.d_in, xw.d_in)
+            Hg.zero_()
+            P.hessian_accumulate(Xd, Hg, workspace=ws_h)
+            out += P.quantize_layers(Wds, Hg, b["bits"], b["group_size"], b["block_size"], 0.01, b["act_order"],
+                                     workspace=ws_q)
+        return out
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"bench: warmup step {i + 1}/{args.warmup} done")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    P.profile_enable(True)
+    P.profile_read(reset=True)
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = P.profile_read(reset=True)
+    P.profile_enable(False)
+    f_h = sum(b["n"] * xw.d_in * (xw.d_in + 1) for xw, *_ in data)
+    f_upd = sum(lw.d_out * lw.d_in * (lw.d_in - 1) for _, lws, *_ in data for lw in lws)
+    f_factor = sum(2 * xw.d_in ** 3 / 3 for xw, *_ in data)
+    n_layers = sum(len(lws) for _, lws, *_ in data)
+    line = {
+        "metric": f"GPTQ transformer-block sweep ms + TFLOP/s (Hessian+update), {args.workload}",
+        "value": (f_h + f_upd) / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16+fp32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: " + "; ".join(
+            f"{xw.name} d_in={xw.d_in} -> " + ", ".join(f"{lw.name} {lw.d_out}x{lw.d_in}" for lw in lws)
+            for xw, lws, *_ in data) + f"; n={b['n']} tokens, {b['bits']}-bit, group {b['group_size']}, "
+            f"block {b['block_size']}, act_order {'on' if b['act_order'] else 'off'}",
+            "layers": n_layers, "inputs": len(data), "parallelism": "single GPU"},
+        "factorizations": {"per_step": len(data), "without_sharing": n_layers,
+                           "factor_ms_per_step": prof["factor"][0] / args.steps,
+                           "flops_per_step": f_factor},
+        "stages": {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
+                   for k, v in prof.items()},
+        "flops": {"hessian": f_h, "update": f_upd},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +330,8 @@ def main():
     import post_weight_quantization_04_amd as P
     from post_weight_quantization_04_amd import synth
 
+    if args.workload in synth.BLOCKS:
+        return run_block(args, P, synth, torch, np)
     wl = synth.WORKLOADS[args.workload]
     dev = "cuda:0"
     log(f"bench: generating {describe(wl)}")

@@ -150,6 +150,36 @@ GPTQ_API gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int6
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Several layers that read the same input (q/k/v of an attention block,
+ * gate/up of an MLP) share one Hessian, hence one order and one inverse
+ * factor: "GPTQ" (wikiprompt.org), "Abordagem Tecnica" (the model is
+ * quantized layer by layer from each layer's own inputs) and "GPTQ (GPT
+ * Quantization)", "Fondation theorique : OBQ" (H depends only on the inputs
+ * X).  Rows are independent given the factor, so this factors H once and
+ * then quantizes each layer exactly as gptq_quantize_layer would (the same
+ * kernels in the same order: the results are bitwise those of one
+ * gptq_quantize_layer call per layer).
+ *   n_layers   1 .. 4096.
+ *   W, d_out, Qpacked, scales, zeros: HOST arrays of n_layers entries (the
+ *              pointers they hold are device pointers; each layer has its own
+ *              d_out and its own outputs, laid out as for
+ *              gptq_quantize_layer).
+ *   perm       one int32 [d_in] for all the layers.
+ *   workspace  gptq_quantize_layers_workspace_size(...) bytes (that of the
+ *              widest layer).
+ * Every other argument, the synchronization and the errors are those of
+ * gptq_quantize_layer.  Layers are processed in order on `stream`.
+ * ------------------------------------------------------------------------- */
+GPTQ_API size_t gptq_quantize_layers_workspace_size(int n_layers, const int64_t *d_out, int64_t d_in, int bits,
+                                                    int group_size, int block_size, int act_order);
+
+GPTQ_API gptq_status gptq_quantize_layers(int n_layers, const void *const *W, gptq_dtype w_dtype,
+                                          const int64_t *d_out, int64_t d_in, const float *H, int bits,
+                                          int group_size, int block_size, float damp, int act_order,
+                                          uint32_t *const *Qpacked, float *const *scales, float *const *zeros,
+                                          int32_t *perm, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Stage 2 alone, for inspection: activation order and the inverse factor.
  * "Algorithme complet (pseudo-code)" steps 1-2 (damping, inverse through
  * Cholesky).  Writes perm (int32 [d_in]) and U (fp32 [d_in][d_in], device):

@@ -25,7 +25,7 @@ __all__ = [
     "GptqError", "lib", "hessian_accumulate", "hessian_workspace_size", "quantize_layer",
     "quantize_layer_workspace_size", "inverse_factor", "packed_words", "num_groups", "QuantizedLayer",
     "LIB_PATH", "F32", "BF16", "profile_enable", "profile_read", "hessian_accumulate_noalloc",
-    "hessian_noalloc_max_d_in", "dequant_matmul", "dequant_matmul_workspace_size",
+    "hessian_noalloc_max_d_in", "dequant_matmul", "dequant_matmul_workspace_size", "quantize_layers",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
@@ -69,6 +69,13 @@ def _load() -> ctypes.CDLL:
                                       c.c_void_p, c.c_int64, c.c_int, c.c_int, c.c_void_p, c.c_int, c.c_void_p,
                                       c.c_size_t, c.c_void_p]
     L.gptq_dequant_matmul.restype = c.c_int
+    L.gptq_quantize_layers_workspace_size.argtypes = [c.c_int, c.c_void_p, c.c_int64, c.c_int, c.c_int, c.c_int,
+                                                      c.c_int]
+    L.gptq_quantize_layers_workspace_size.restype = c.c_size_t
+    L.gptq_quantize_layers.argtypes = [c.c_int, c.c_void_p, c.c_int, c.c_void_p, c.c_int64, c.c_void_p, c.c_int,
+                                       c.c_int, c.c_int, c.c_float, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p,
+                                       c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+    L.gptq_quantize_layers.restype = c.c_int
     L.gptq_inverse_factor.argtypes = [c.c_void_p, c.c_int64, c.c_float, c.c_int, c.c_void_p, c.c_void_p,
                                       c.c_void_p, c.c_size_t, c.c_void_p]
     L.gptq_inverse_factor.restype = c.c_int
@@ -237,6 +244,7 @@ class QuantizedLayer:
     bits: int
     group_size: int     # effective group size
     d_in: int
+    act_order: bool = True   # False: perm is the identity (products then skip the gather)
 
 
 def quantize_layer(W, H, bits: int = 4, group_size: int = 128, block_size: int = 128, damp: float = 0.01,
@@ -264,18 +272,64 @@ def quantize_layer(W, H, bits: int = 4, group_size: int = 128, block_size: int =
                                    zr.data_ptr(), pm.data_ptr(), ws.data_ptr() if ws is not None else None,
                                    0 if ws is None else ws.numel(), _stream_ptr(stream)))
     g_eff = d_in if (group_size == -1 or group_size >= d_in) else group_size
-    return QuantizedLayer(q, sc, zr, pm, bits, g_eff, d_in)
+    return QuantizedLayer(q, sc, zr, pm, bits, g_eff, d_in, bool(act_order))
+
+
+def quantize_layers(Ws, H, bits: int = 4, group_size: int = 128, block_size: int = 128, damp: float = 0.01,
+                    act_order: bool = False, workspace=None, stream=None):
+    """Quantize several layers that share the input, hence H (gptq_quantize_layers):
+    one factorization, then each W [d_out_l, d_in] as quantize_layer would.
+    Returns a list of QuantizedLayer sharing one perm."""
+    torch = _torch()
+    Ws = list(Ws)
+    if not Ws:
+        raise ValueError("no layers")
+    _require(H, "H", dtype=torch.float32, ndim=2)
+    d_in = H.shape[0]
+    code = None
+    for W in Ws:
+        _require(W, "W", ndim=2)
+        if W.shape[1] != d_in:
+            raise ValueError(f"every W must have {d_in} columns")
+        c = _dtype_code(W)
+        if code is not None and c != code:
+            raise TypeError("every W must have the same dtype")
+        code = c
+    n = len(Ws)
+    G = num_groups(d_in, group_size)
+    nw = packed_words(d_in, bits)
+    if G < 1 or nw < 0:
+        raise GptqError(1, "invalid group_size or bits")
+    dev = Ws[0].device
+    d_outs = (ctypes.c_int64 * n)(*[W.shape[0] for W in Ws])
+    outs = [(torch.empty((nw, W.shape[0]), dtype=torch.int32, device=dev),
+             torch.empty((G, W.shape[0]), dtype=torch.float32, device=dev),
+             torch.empty((G, W.shape[0]), dtype=torch.float32, device=dev)) for W in Ws]
+    pm = torch.empty((d_in,), dtype=torch.int32, device=dev)
+    ptrs = lambda xs: (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    need = int(_lib().gptq_quantize_layers_workspace_size(n, d_outs, d_in, bits, group_size, block_size,
+                                                           int(act_order)))
+    ws = _workspace(need, dev, workspace)
+    _check(_lib().gptq_quantize_layers(n, ptrs(Ws), code, d_outs, d_in, H.data_ptr(), bits, group_size, block_size,
+                                       float(damp), int(bool(act_order)), ptrs([o[0] for o in outs]),
+                                       ptrs([o[1] for o in outs]), ptrs([o[2] for o in outs]), pm.data_ptr(),
+                                       ws.data_ptr() if ws is not None else None, 0 if ws is None else ws.numel(),
+                                       _stream_ptr(stream)))
+    g_eff = d_in if (group_size == -1 or group_size >= d_in) else group_size
+    return [QuantizedLayer(o[0], o[1], o[2], pm, bits, g_eff, d_in, bool(act_order)) for o in outs]
 
 
 def dequant_matmul_workspace_size(m, d_out, d_in, bits, group_size) -> int:
     return int(_lib().gptq_dequant_matmul_workspace_size(m, d_out, d_in, bits, group_size))
 
 
-def dequant_matmul(A, q: "QuantizedLayer", out_dtype=None, workspace=None, stream=None, use_perm: bool = True):
+def dequant_matmul(A, q: "QuantizedLayer", out_dtype=None, workspace=None, stream=None, use_perm=None):
     """Y = A W_hat^T on the packed layer q (gptq_dequant_matmul).  A: [m, d_in]
     bfloat16/float32 activations in the original column order; returns Y
     [m, d_out] in out_dtype (float32 by default, or bfloat16).  A workspace
-    passed in must have been zeroed before its first use (calls leave it so)."""
+    passed in must have been zeroed before its first use (calls leave it so).
+    use_perm: gather A through q.perm (default: when q was quantized with
+    act-order; otherwise perm is the identity and is not passed)."""
     torch = _torch()
     _require(A, "A", ndim=2)
     m, d_in = A.shape
@@ -283,6 +337,8 @@ def dequant_matmul(A, q: "QuantizedLayer", out_dtype=None, workspace=None, strea
         raise ValueError(f"A has {d_in} columns, the layer {q.d_in}")
     d_out = q.scales.shape[1]
     out_dtype = out_dtype or torch.float32
+    if use_perm is None:
+        use_perm = q.act_order
     Y = torch.empty((m, d_out), dtype=out_dtype, device=A.device)
     need = dequant_matmul_workspace_size(m, d_out, d_in, q.bits, q.group_size)
     # zeroed before its first use (completion counters); calls leave it so

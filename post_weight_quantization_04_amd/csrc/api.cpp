@@ -181,6 +181,70 @@ gptq_status run_factor(const float *H, int64_t d, float damp, int act_order, int
     return GPTQ_OK;
 }
 
+// Stages 3-5 for one layer on the factor already in the workspace: gather
+// the layer's weights into processing order, the batched in-block and
+// trailing updates, packing.
+gptq_status quantize_rows(const void *W, int w_bf16, int64_t d_out, int64_t d_in, int bits, int group, int block_int,
+                          const int32_t *perm, uint32_t *Qpacked, float *scales, float *zeros, Workspace &w,
+                          hipStream_t st) {
+    {
+        StageTimer t(2, st);
+        HIPCHECK(gptq::prep_gather_w(W, w_bf16, perm, d_out, d_in, w.Wp, st));
+    }
+    gptq::QuantArgs qa{};
+    qa.Wp = w.Wp;
+    qa.U = w.R;
+    qa.ud = w.ud;
+    qa.uinv = w.uinv;
+    qa.E = w.E;
+    qa.codes = w.codes;
+    qa.scales = scales;
+    qa.zeros = zeros;
+    qa.d_out = d_out;
+    qa.d_in = d_in;
+    qa.bits = bits;
+    qa.group = group;
+    qa.block = block_int;
+    // Blocks go in batches of far_blocks(B); the errors of a batch's blocks are
+    // stacked in E (block t of the batch at rows t*B..).  One in-block launch
+    // takes the whole batch, each block first applying the batch's earlier
+    // errors to its own columns (the near update); then one product applies
+    // all of them to every column beyond.  A group wider than a block takes
+    // its parameters from all its columns at its start, so a batch also ends
+    // before such a group begins.
+    const int64_t B = block_int;
+    for (int64_t pend0 = 0; pend0 < d_in;) {
+        // one batch: up to far_blocks(B) blocks, ending early after a block whose
+        // end starts a group wider than a block
+        int nblk = 0;
+        int64_t e = pend0;
+        while (nblk < gptq::far_blocks(B) && e < d_in) {
+            e = std::min<int64_t>(e + B, d_in);
+            ++nblk;
+            if (group > B && e % group == 0) break;
+        }
+        {
+            StageTimer t(5, st);
+            gptq::QuantArgs qb = qa;
+            qb.E = w.E;
+            qb.En = w.E;
+            qb.near_row0 = pend0;
+            HIPCHECK(gptq::quant_block_launch(qb, pend0, nblk, B, st));
+        }
+        if (e >= d_in) break;
+        {
+            StageTimer t(6, st);
+            HIPCHECK(gptq::trail_launch(qa, pend0, e - pend0, e, d_in, st));
+        }
+        pend0 = e;
+    }
+    {
+        StageTimer t(7, st);
+        HIPCHECK(gptq::pack_launch(w.codes, d_out, d_in, bits, Qpacked, st));
+    }
+    return GPTQ_OK;
+}
+
 // The factorization's pivot flag, read once everything has been enqueued so
 // that the device never idles waiting for the host in the middle of a layer.
 // On a bad pivot the later stages ran on non-finite values; they index no
@@ -365,81 +429,60 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
                                 int bits, int group_size, int block_size, float damp, int act_order,
                                 uint32_t *Qpacked, float *scales, float *zeros, int32_t *perm, void *workspace,
                                 size_t workspace_bytes, void *stream) {
+    return gptq_quantize_layers(1, &W, w_dtype, &d_out, d_in, H, bits, group_size, block_size, damp, act_order,
+                                &Qpacked, &scales, &zeros, perm, workspace, workspace_bytes, stream);
+}
+
+size_t gptq_quantize_layers_workspace_size(int n_layers, const int64_t *d_out, int64_t d_in, int bits, int group_size,
+                                           int block_size, int act_order) {
+    if (n_layers < 1 || !d_out) return 0;
+    int64_t dmax = 0;
+    for (int l = 0; l < n_layers; ++l) dmax = std::max(dmax, d_out[l]);
+    return gptq_quantize_layer_workspace_size(dmax, d_in, bits, group_size, block_size, act_order);
+}
+
+gptq_status gptq_quantize_layers(int n_layers, const void *const *W, gptq_dtype w_dtype, const int64_t *d_out,
+                                 int64_t d_in, const float *H, int bits, int group_size, int block_size, float damp,
+                                 int act_order, uint32_t *const *Qpacked, float *const *scales, float *const *zeros,
+                                 int32_t *perm, void *workspace, size_t workspace_bytes, void *stream) {
     g_err.clear();
-    LayerShape L{};
-    gptq_status s = check_layer(d_out, d_in, bits, group_size, block_size, L);
-    if (s != GPTQ_OK) return s;
+    if (n_layers < 1 || n_layers > 4096) return fail(GPTQ_EINVAL, "n_layers must be in [1, 4096] (got %d)", n_layers);
+    if (!W || !d_out || !Qpacked || !scales || !zeros) return fail(GPTQ_EINVAL, "a required array is NULL");
+    LayerShape Lmax{};
+    int64_t dmax = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        LayerShape Ll{};
+        gptq_status s = check_layer(d_out[l], d_in, bits, group_size, block_size, Ll);
+        if (s != GPTQ_OK) return s;
+        if (!W[l] || !Qpacked[l] || !scales[l] || !zeros[l])
+            return fail(GPTQ_EINVAL, "a required pointer of layer %d is NULL", l);
+        if (d_out[l] > dmax) {
+            dmax = d_out[l];
+            Lmax = Ll;
+        }
+    }
     if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "w_dtype must be GPTQ_F32 or GPTQ_BF16");
     if (!std::isfinite(damp) || damp < 0.f) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
     if (act_order != 0 && act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
-    if (!W || !H || !Qpacked || !scales || !zeros || !perm) return fail(GPTQ_EINVAL, "a required pointer is NULL");
-    const size_t need = layout(L, nullptr).bytes;
+    if (!H || !perm) return fail(GPTQ_EINVAL, "a required pointer is NULL");
+    const size_t need = layout(Lmax, nullptr).bytes;
     if (!workspace || workspace_bytes < need)
         return fail(GPTQ_ENOMEM, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     hipStream_t st = (hipStream_t)stream;
-    Workspace w = layout(L, (char *)workspace);
+    // every buffer sized for the widest layer serves the narrower ones too
+    // (their row strides are their own d_out)
+    Workspace w = layout(Lmax, (char *)workspace);
 
-    s = run_factor(H, d_in, damp, act_order, perm, w, st);
+    gptq_status s = run_factor(H, d_in, damp, act_order, perm, w, st);
     if (s != GPTQ_OK) return s;
     {
         StageTimer t(4, st);
         HIPCHECK(gptq::factor_flip(w.R, d_in, w.ud, w.uinv, 0, st));
     }
-    {
-        StageTimer t(2, st);
-        HIPCHECK(gptq::prep_gather_w(W, w_dtype == GPTQ_BF16, perm, d_out, d_in, w.Wp, st));
-    }
-
-    gptq::QuantArgs qa{};
-    qa.Wp = w.Wp;
-    qa.U = w.R;
-    qa.ud = w.ud;
-    qa.uinv = w.uinv;
-    qa.E = w.E;
-    qa.codes = w.codes;
-    qa.scales = scales;
-    qa.zeros = zeros;
-    qa.d_out = d_out;
-    qa.d_in = d_in;
-    qa.bits = bits;
-    qa.group = L.group;
-    qa.block = L.block_int;
-    // Blocks go in batches of far_blocks(B); the errors of a batch's blocks are
-    // stacked in E (block t of the batch at rows t*B..).  One in-block launch
-    // takes the whole batch, each block first applying the batch's earlier
-    // errors to its own columns (the near update); then one product applies
-    // all of them to every column beyond.  A group wider than a block takes
-    // its parameters from all its columns at its start, so a batch also ends
-    // before such a group begins.
-    const int64_t B = L.block_int;
-    for (int64_t pend0 = 0; pend0 < d_in;) {
-        // one batch: up to far_blocks(B) blocks, ending early after a block whose
-        // end starts a group wider than a block
-        int nblk = 0;
-        int64_t e = pend0;
-        while (nblk < gptq::far_blocks(B) && e < d_in) {
-            e = std::min<int64_t>(e + B, d_in);
-            ++nblk;
-            if (L.group > B && e % L.group == 0) break;
-        }
-        {
-            StageTimer t(5, st);
-            gptq::QuantArgs qb = qa;
-            qb.E = w.E;
-            qb.En = w.E;
-            qb.near_row0 = pend0;
-            HIPCHECK(gptq::quant_block_launch(qb, pend0, nblk, B, st));
-        }
-        if (e >= d_in) break;
-        {
-            StageTimer t(6, st);
-            HIPCHECK(gptq::trail_launch(qa, pend0, e - pend0, e, d_in, st));
-        }
-        pend0 = e;
-    }
-    {
-        StageTimer t(7, st);
-        HIPCHECK(gptq::pack_launch(w.codes, d_out, d_in, bits, Qpacked, st));
+    for (int l = 0; l < n_layers; ++l) {
+        s = quantize_rows(W[l], w_dtype == GPTQ_BF16, d_out[l], d_in, bits, Lmax.group, Lmax.block_int, perm,
+                          Qpacked[l], scales[l], zeros[l], w, st);
+        if (s != GPTQ_OK) return s;
     }
     return read_pivot_flag(w, st);
 }

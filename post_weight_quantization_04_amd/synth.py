@@ -76,6 +76,44 @@ WORKLOADS = {
 }
 
 
+# Transformer blocks: the linear layers of one Llama block grouped by the input
+# they read (layers of a group share that input's Hessian).  Each entry:
+# (input, d_in, x law, x tag, [(layer, d_out, w tag), ...]).  The attention
+# input uses q_proj's activation draws and the MLP's inner activations
+# down_proj's; the other inputs have tags of their own.  Weights follow the
+# q_proj law (the 70B block the 70B down_proj's).
+BLOCKS = {
+    "llama7b_block": dict(n=262144, bits=4, group_size=128, block_size=128, act_order=False, w_std=0.02,
+                          w_outlier_frac=0.001, groups=[
+        ("attn_in", 4096, "lognormal_ch", 2, [("q_proj", 4096, 31), ("k_proj", 4096, 32), ("v_proj", 4096, 33)]),
+        ("attn_out", 4096, "lognormal_ch", 21, [("o_proj", 4096, 34)]),
+        ("mlp_in", 4096, "lognormal_ch", 22, [("gate_proj", 11008, 35), ("up_proj", 11008, 36)]),
+        ("mlp_mid", 11008, "student_t", 3, [("down_proj", 4096, 37)]),
+    ]),
+    "llama70b_block": dict(n=131072, bits=4, group_size=128, block_size=256, act_order=False, w_std=0.015,
+                           w_outlier_frac=0.0, groups=[
+        ("attn_in", 8192, "lognormal_ch", 51, [("q_proj", 8192, 61), ("k_proj", 1024, 62), ("v_proj", 1024, 63)]),
+        ("attn_out", 8192, "lognormal_ch", 52, [("o_proj", 8192, 64)]),
+        ("mlp_in", 8192, "lognormal_ch", 53, [("gate_proj", 28672, 65), ("up_proj", 28672, 66)]),
+        ("mlp_mid", 28672, "lognormal_ch", 5, [("down_proj", 8192, 67)]),
+    ]),
+}
+
+
+def block_workloads(name: str, n: int | None = None):
+    """[(input workload, [layer workloads])] of a block; the input workload
+    carries the X law and the layer workloads the W law (same d_in)."""
+    b = BLOCKS[name]
+    n = n or b["n"]
+    out = []
+    for inp, d_in, law, xtag, layers in b["groups"]:
+        xw = Workload(xtag, inp, 1, d_in, n, "bf16", b["bits"], b["group_size"], b["block_size"], 0.01,
+                      b["act_order"], b["w_std"], b["w_outlier_frac"], law)
+        lws = [replace(xw, tag=wtag, name=lname, d_out=d_out) for lname, d_out, wtag in layers]
+        out.append((xw, lws))
+    return out
+
+
 def _rng(tag: int, stream: int, index: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([tag, stream, index])))
 

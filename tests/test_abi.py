@@ -159,3 +159,29 @@ def test_dequant_matmul_rejects_bad_arguments():
     assert call(wsb=16) == 4
     assert P.dequant_matmul_workspace_size(0, 4096, 4096, 4, 128) == 0
     assert P.dequant_matmul_workspace_size(1, 4096, 4096, 5, 128) == 0
+
+
+def test_quantize_layers_rejects_bad_arguments():
+    L = P.lib
+    n = 2
+    arr = lambda: (ctypes.c_void_p * n)(FAKE.value, FAKE.value)
+    dout = (ctypes.c_int64 * n)(64, 32)
+
+    def call(**kw):
+        a = dict(n=n, W=arr(), dt=P.BF16, dout=dout, d_in=256, H=FAKE, bits=4, g=128, B=128, damp=0.01, act=0,
+                 Q=arr(), S=arr(), Z=arr(), perm=FAKE, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return L.gptq_quantize_layers(a["n"], a["W"], a["dt"], a["dout"], a["d_in"], a["H"], a["bits"], a["g"],
+                                      a["B"], a["damp"], a["act"], a["Q"], a["S"], a["Z"], a["perm"], a["ws"],
+                                      a["wsb"], None)
+
+    assert call(n=0) == 1
+    assert call(W=None) == 1
+    assert call(W=(ctypes.c_void_p * n)(FAKE.value, None)) == 1
+    assert call(dout=(ctypes.c_int64 * n)(64, 0)) == 1
+    assert call(bits=5) == 1
+    assert call(perm=None) == 1
+    assert call(wsb=1024) == 4
+    # the workspace is that of the widest layer
+    assert L.gptq_quantize_layers_workspace_size(n, dout, 256, 4, 128, 128, 0) == \
+        P.quantize_layer_workspace_size(64, 256, 4, 128, 128, 0)

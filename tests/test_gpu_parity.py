@@ -364,3 +364,65 @@ def test_full_layer_down70b_rows():
     torch.cuda.empty_cache()
     res = replay_rows("down70b", wl, W, X, q, one_row_per_group(wl.d_out, 2), 2)
     assert res["ok"], res
+
+
+# ---------------------------------------------------------------------------
+# layers sharing one input: one factorization for several layers
+# ---------------------------------------------------------------------------
+def _q_equal(a, b):
+    return all(torch.equal(x, y) for x, y in ((a.qpacked, b.qpacked), (a.scales, b.scales), (a.zeros, b.zeros),
+                                              (a.perm, b.perm)))
+
+
+@pytest.mark.parametrize("act", [False, True])
+def test_quantize_layers_equals_one_call_per_layer(act):
+    """q/k/v-like layers of different widths reading one input: the shared
+    factorization gives bitwise the results of one gptq_quantize_layer call
+    per layer, and the narrow middle layer matches the oracle."""
+    d_in, n = 640, 4096
+    xw = synth.WORKLOADS["q_proj"].with_shape(401, 8, d_in, n)
+    X = synth.make_x(xw)
+    Hg = gpu_hessian(X, "bf16")
+    Ws = [synth.make_w(synth.WORKLOADS["q_proj"].with_shape(402 + i, d, d_in, n)) for i, d in enumerate((200, 64, 300))]
+    Wd = [to_dev(W, "bf16") for W in Ws]
+    qs = P.quantize_layers(Wd, Hg, 4, 128, 128, 0.01, act)
+    torch.cuda.synchronize()
+    for Wi, q in zip(Wd, qs):
+        q1 = P.quantize_layer(Wi, Hg, 4, 128, 128, 0.01, act)
+        torch.cuda.synchronize()
+        assert _q_equal(q, q1)
+    H = O.hessian([X], "bf16", d_in)
+    q = qs[1]
+    res = C.check_layer(O.widen(Ws[1], "bf16"), H, 4, 128, 128, 0.01, act, q.qpacked.cpu().numpy().view(np.uint32),
+                        q.scales.cpu().numpy(), q.zeros.cpu().numpy(), q.perm.cpu().numpy())
+    assert res["ok"], res
+
+
+def test_block_sweep_layers_match_the_oracle():
+    """A Llama-shaped block at reduced size (d_model 512, d_ff 1376, 4096
+    tokens): per input, the GPU Hessian and gptq_quantize_layers on the layers
+    reading it; every layer checked against the oracle on its own input's
+    float64 Hessian (one row of every 16-row work group)."""
+    shapes = {"attn_in": 512, "attn_out": 512, "mlp_in": 512, "mlp_mid": 1376}
+    outs = {"q_proj": 512, "k_proj": 128, "v_proj": 128, "o_proj": 512, "gate_proj": 1376, "up_proj": 1376,
+            "down_proj": 512}
+    for xw, lws in synth.block_workloads("llama7b_block", n=4096):
+        d_in = shapes[xw.name]
+        xw = xw.with_shape(xw.tag + 700, 1, d_in, 4096)
+        lws = [lw.with_shape(lw.tag + 700, outs[lw.name], d_in, 4096) for lw in lws]
+        say(f"block input {xw.name} d_in={d_in}: " + ", ".join(lw.name for lw in lws))
+        X = synth.make_x(xw)
+        Hg = gpu_hessian(X, "bf16")
+        Ws = [synth.make_w(lw) for lw in lws]
+        qs = P.quantize_layers([to_dev(W, "bf16") for W in Ws], Hg, xw.bits, xw.group_size, xw.block_size, xw.damp,
+                               xw.act_order)
+        torch.cuda.synchronize()
+        H = O.hessian([X], "bf16", d_in)
+        for lw, W, q in zip(lws, Ws, qs):
+            rows = one_row_per_group(lw.d_out, 5)
+            res = C.check_layer(O.widen(W[rows], "bf16"), H, xw.bits, xw.group_size, xw.block_size, xw.damp,
+                                xw.act_order, q.qpacked.cpu().numpy().view(np.uint32)[:, rows],
+                                q.scales.cpu().numpy()[:, rows], q.zeros.cpu().numpy()[:, rows], q.perm.cpu().numpy())
+            say(f"  {lw.name} {lw.d_out}x{d_in}: ok={res['ok']} exempt {res.get('exempt_codes')} "
+                f"loss rel {res.get('loss_rel', float('nan')):.2e}")
+            assert res["ok"], (lw.name, res)
