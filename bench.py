@@ -165,6 +165,25 @@ def gemv_bench(P, torch, wl, q, Xd, calls=200):
         log(f"bench: dequant product m={m}: {us:.2f} us/call, {gbs:.0f} GB/s")
     out["bound"] = "hbm"
     out["layer"] = f"{wl.d_out}x{wl.d_in} {q.bits}-bit group {q.group_size}, the layer just quantized"
+    # prefill shape: the wide path (bf16 matrix cores), bound by them
+    m = min(4096, Xd.shape[0])
+    if Xd.dtype == torch.bfloat16 and wl.d_in % 8 == 0:
+        A = Xd[:m].contiguous()
+        ws = torch.zeros(max(P.dequant_matmul_workspace_size(m, wl.d_out, wl.d_in, q.bits, q.group_size), 1),
+                         dtype=torch.uint8, device=A.device)
+        P.dequant_matmul(A, q, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(20):
+            P.dequant_matmul(A, q, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        tf = 2.0 * m * wl.d_out * wl.d_in / (us * 1e-6) / 1e12
+        out[f"m{m}"] = {"us_per_call": us, "tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS,
+                        "bound": "mfma"}
+        log(f"bench: dequant product m={m}: {us:.1f} us/call, {tf:.0f} TFLOP/s")
     return out
 
 

@@ -209,12 +209,16 @@ GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float dam
  *            (identity, as act_order = 0 writes it).
  *   Y        device, [m][d_out], y_dtype F32 or BF16 (rounded to nearest
  *            even from the fp32 result).
- * Codes are multiplied in fp32 with the fp32-widened activations; every 16
- * codes the group's scale and zero point are applied as
- * s * (sum A q) - s z * (sum A), and the partial sums of the k-ranges are
- * added in a fixed order (deterministic).  Up to 8 rows of A per launch (the
- * decode shape, bound by reading the packed weights); larger m runs in
- * chunks of 8.
+ * Two paths, both deterministic:
+ *   - skinny (m < 16, or fp32 activations, or d_in % 8 != 0; the decode
+ *     shape, bound by reading the packed weights): codes are multiplied in
+ *     fp32 with the fp32-widened activations, every 16 codes the group's
+ *     scale and zero point are applied as s * (sum A q) - s z * (sum A), and
+ *     the k-ranges' partial sums are added in a fixed order; up to 8 rows of
+ *     A per launch, larger m in chunks of 8;
+ *   - wide (m >= 16 bf16 rows, d_in % 8 == 0; prefill): per group the exact
+ *     integers q - z meet the activations on bf16 matrix cores (every product
+ *     exact, fp32 sums), and Y += s * (group sum).
  * workspace  device scratch of gptq_dequant_matmul_workspace_size(m, d_out,
  *            d_in, bits, group_size) bytes (0 when m == 0; may then be NULL).
  *            It holds the k-ranges' partial sums and one completion counter

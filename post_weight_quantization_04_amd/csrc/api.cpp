@@ -521,6 +521,7 @@ gptq_status gptq_dequant_matmul(const void *A, gptq_dtype a_dtype, int64_t m, in
     a.y_bf16 = y_dtype == GPTQ_BF16;
     a.part = (float *)workspace;
     a.counters = (int32_t *)((char *)workspace + wl.counters_off);
+    a.ap = (uint16_t *)((char *)workspace + wl.ap_off);
     a.m = m;
     a.d_in = d_in;
     a.d_out = d_out;

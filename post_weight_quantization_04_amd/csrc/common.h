@@ -142,12 +142,13 @@ struct DequantArgs {
     int y_bf16;             // Y is bf16 (else fp32)
     float *part;            // workspace: partial sums of the k-ranges
     int32_t *counters;      // workspace: one per 256-row tile, zero between calls
+    uint16_t *ap;           // workspace: activations in processing order (wide path)
     int64_t m, d_in, d_out;
     int bits, group;        // group: effective group size
     int ngroups;
 };
 struct DequantWs {
-    size_t counters_off, counters_bytes, bytes;
+    size_t counters_off, counters_bytes, ap_off, bytes;
 };
 DequantWs dequant_ws_layout(int64_t m, int64_t d_out, int64_t d_in, int bits);
 hipError_t dequant_matmul_launch(const DequantArgs &a, hipStream_t st);

@@ -360,10 +360,213 @@ hipError_t launch_gemv_bits(const DequantArgs &a, hipStream_t st) {
     return hipSuccess;
 }
 
+
+// code k (0..31, a constant after unrolling) of a unit held in BITS words
+template <int BITS>
+__device__ __forceinline__ unsigned unit_code_w(const unsigned (&w)[BITS], int k) {
+    const int pos = BITS * k, j = pos >> 5, sh = pos & 31;
+    if (sh + BITS <= 32) return __builtin_amdgcn_ubfe(w[j], sh, BITS);
+    return __builtin_amdgcn_alignbit(w[j + 1 < BITS ? j + 1 : j], w[j], sh) & ((1u << BITS) - 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Wide path (m >= 16 bf16 activation rows; prefill): bf16 MFMA on exact
+// integer weights.  For every group, D = A_p[:, group] (q - z)[group, :]^T is
+// formed with v_mfma_f32_32x32x16_bf16: q - z is an integer in [-255, 255]
+// and exact in bf16, every product of two bf16 values is exact in fp32, and
+// D accumulates in fp32; at the group's end Y += s D (one fp32 fma per
+// output and group).  A work group (8 waves, 4 x 2, each 64 x 64 as 2 x 2
+// tiles of 32 x 32) owns 256 x 128 of Y and walks k in chunks of 64: the
+// chunk's activations (256 x 64 bf16) and its weights as q - z in bf16
+// (128 x 64; each thread dequantizes 16 codes of one row) go through LDS,
+// the next chunk's loads issued before the current chunk's products; staged
+// rows are padded by 8 bf16 so that the 16-byte operand reads of a wave fall
+// on distinct banks.  The chunk's scales are staged with them.  Activations
+// of an act-order layer are first gathered into processing order into the
+// workspace by a separate kernel.
+// ---------------------------------------------------------------------------
+constexpr int GM_BM = 256, GM_BN = 128, GM_KC = 64;
+constexpr int GM_LDA = GM_KC + 8;            // bf16 per staged row (padding)
+constexpr int GM_MAXG = GM_KC / 16;          // groups a chunk can touch (g >= 16)
+constexpr int GM_MIN_M = 16;                 // fewest activation rows for the wide path
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// A_p[i][k] = A[i][perm[k]] (bf16), the activations in processing order
+__global__ __launch_bounds__(256) void dq_permute_kernel(const uint16_t *__restrict__ A,
+                                                         const int32_t *__restrict__ perm,
+                                                         uint16_t *__restrict__ Ap, int64_t m, int64_t d_in) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= m * d_in) return;
+    const int64_t i = idx / d_in, k = idx - i * d_in;
+    Ap[idx] = A[i * d_in + perm[k]];
+}
+
+// d_in % 8 == 0 (whole 16-byte pieces of activation rows)
+template <int BITS>
+__global__ __launch_bounds__(512) void dq_gemm_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Q,
+                                                      const float *__restrict__ scales,
+                                                      const float *__restrict__ zeros, void *__restrict__ Y,
+                                                      int y_bf16, int64_t m, int64_t d_in, int64_t d_out, int g,
+                                                      int ngroups, int64_t nwords) {
+    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][GM_BM * GM_LDA];
+    __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][GM_BN * GM_LDA];
+    __shared__ float s_lds[2][GM_MAXG * GM_BN];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.x * GM_BM, n0 = (int64_t)blockIdx.y * GM_BN;
+    const int nchunks = (int)((d_in + GM_KC - 1) / GM_KC);
+
+    // staging roles.  Activations: row tid / 2, pieces 4 (tid % 2) .. +3 (8
+    // bf16 each).  Weights: row tid % 128, codes 16 q .. 16 q + 15 of the
+    // chunk (q = tid / 128), from the unit's words.  Scales: slot tid / 128 of
+    // row tid % 128.
+    const int64_t arow = m0 + (tid >> 1);
+    const int apiece = 4 * (tid & 1);
+    const int bn = tid & (GM_BN - 1), bq = tid >> 7;
+    const int64_t nrow = n0 + bn;
+    u32x4 ra[4];
+    unsigned rw[BITS];
+    float rz = 0.f, rs = 0.f;
+    auto load_chunk = [&](int c) {
+        const int64_t k0 = (int64_t)c * GM_KC;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t k = k0 + 8 * (apiece + q);
+            ra[q] = (arow < m && k < d_in) ? *(const u32x4 *)(A + arow * d_in + k) : u32x4{0u, 0u, 0u, 0u};
+        }
+        const int64_t u = (k0 >> 5) + (bq >> 1);   // 32-code unit of this thread's codes
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            const int64_t wi = u * BITS + b;
+            rw[b] = (nrow < d_out && wi < nwords) ? Q[wi * d_out + nrow] : 0u;
+        }
+        const int64_t gz = std::min<int64_t>((k0 + 16 * bq) / g, ngroups - 1);
+        rz = nrow < d_out ? zeros[gz * d_out + nrow] : 0.f;
+        const int64_t gs = std::min<int64_t>(k0 / g + bq, ngroups - 1);
+        rs = nrow < d_out ? scales[gs * d_out + nrow] : 0.f;
+    };
+    auto store_chunk = [&](int buf) {
+        uint16_t *ad = a_lds[buf] + (tid >> 1) * GM_LDA + 8 * apiece;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *(u32x4 *)(ad + 8 * q) = ra[q];
+        // codes 16 (bq % 2) .. +15 of the unit as q - z in bf16
+        unsigned pk[8];
+        const int c0 = 16 * (bq & 1);
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 2) {
+            const float v0 = (float)unit_code_w<BITS>(rw, c0 + kk) - rz;
+            const float v1 = (float)unit_code_w<BITS>(rw, c0 + kk + 1) - rz;
+            const bf16x2 p = {(__bf16)v0, (__bf16)v1};
+            pk[kk >> 1] = __builtin_bit_cast(unsigned, p);
+        }
+        uint16_t *bd = b_lds[buf] + bn * GM_LDA + 16 * bq;
+        *(u32x4 *)(bd) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        *(u32x4 *)(bd + 8) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+        s_lds[buf][bq * GM_BN + bn] = rs;
+    };
+
+    f32x16 acc[2][2], dg[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            acc[a][b] = f32x16{};
+            dg[a][b] = f32x16{};
+        }
+    // operand reads: lane l supplies row / column l % 32, k 8 (l / 32) .. +7
+    const int orow = lane & 31, ok = 8 * (lane >> 5);
+
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nchunks) load_chunk(c + 1);   // in flight during this chunk's products
+        const int64_t k0 = (int64_t)c * GM_KC;
+        const uint16_t *ab = a_lds[buf] + (wm * 64 + orow) * GM_LDA + ok;
+        const uint16_t *bb = b_lds[buf] + (wn * 64 + orow) * GM_LDA + ok;
+#pragma unroll
+        for (int ks = 0; ks < GM_KC / 16; ++ks) {
+            const int64_t k = k0 + 16 * ks;
+            if (k >= d_in) break;   // uniform
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) fa[a] = *(const bf16x8 *)(ab + a * 32 * GM_LDA + 16 * ks);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) fb[b] = *(const bf16x8 *)(bb + b * 32 * GM_LDA + 16 * ks);
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    dg[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], dg[a][b], 0, 0, 0);
+            // a group ends after this k step: Y += s D, D = 0 (uniform)
+            const int64_t kn = k + 16;
+            if (kn >= d_in || kn % g == 0) {
+                const int slot = (int)(k / g - k0 / g);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const float sc = s_lds[buf][slot * GM_BN + wn * 64 + 32 * b + orow];
+#pragma unroll
+                    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(sc, dg[a][b][r], acc[a][b][r]);
+                        dg[a][b] = f32x16{};
+                    }
+                }
+            }
+        }
+        __syncthreads();   // every wave is done with the other buffer's previous chunk
+        if (c + 1 < nchunks) store_chunk(buf ^ 1);
+        __syncthreads();
+    }
+    // Y: tile (a, b) of wave (wm, wn), register 4 i + j <-> row 8 i + 4 (l / 32) + j, column l % 32
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int64_t n = n0 + wn * 64 + 32 * b + orow;
+            if (n >= d_out) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 64 + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row >= m) continue;
+                const float v = acc[a][b][r];
+                if (y_bf16) {
+                    const unsigned u = __builtin_bit_cast(unsigned, v);
+                    ((uint16_t *)Y)[row * d_out + n] = (uint16_t)((u + ((u >> 16) & 1u) + 0x7FFFu) >> 16);
+                } else {
+                    ((float *)Y)[row * d_out + n] = v;
+                }
+            }
+        }
+}
+
+template <int BITS>
+hipError_t launch_gemm_bits(const DequantArgs &a, hipStream_t st) {
+    const uint16_t *A = (const uint16_t *)a.A;
+    if (a.perm) {
+        const int64_t n = a.m * a.d_in;
+        dq_permute_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(A, a.perm, a.ap, a.m, a.d_in);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        A = a.ap;
+    }
+    const dim3 grid((unsigned)cdiv(a.m, GM_BM), (unsigned)cdiv(a.d_out, GM_BN));
+    const int64_t nwords = cdiv((int64_t)BITS * a.d_in, 32);
+    dq_gemm_kernel<BITS><<<grid, 512, 0, st>>>(A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.m, a.d_in, a.d_out,
+                                               a.group, a.ngroups, nwords);
+    return hipGetLastError();
+}
 }  // namespace
 
-// Workspace: the partial sums of the widest launch ([nsplit][M][d_out] fp32),
-// then one counter per row tile (zero between calls).
+// The wide (MFMA) path takes bf16 activations with at least GM_MIN_M rows
+// and whole 16-byte row pieces; everything else runs on the skinny path.
+bool dequant_wide(int64_t m, int a_bf16, int64_t d_in) { return m >= GM_MIN_M && a_bf16 && d_in % 8 == 0; }
+
+// Workspace: the skinny path's partial sums of its widest launch
+// ([nsplit][M][d_out] fp32), then one counter per row tile (zero between
+// calls), then (m >= GM_MIN_M) room for the activations in processing order.
 DequantWs dequant_ws_layout(int64_t m, int64_t d_out, int64_t d_in, int bits) {
     DequantWs w{};
     size_t part = 0;
@@ -374,11 +577,22 @@ DequantWs dequant_ws_layout(int64_t m, int64_t d_out, int64_t d_in, int bits) {
     }
     w.counters_off = align256(part);
     w.counters_bytes = (size_t)cdiv(d_out, GV_ROWS) * sizeof(int32_t);
-    w.bytes = m > 0 ? align256(w.counters_off + w.counters_bytes) : 0;
+    w.ap_off = align256(w.counters_off + w.counters_bytes);
+    const size_t ap = m >= GM_MIN_M ? (size_t)m * d_in * sizeof(uint16_t) : 0;
+    w.bytes = m > 0 ? align256(w.ap_off + ap) : 0;
     return w;
 }
 
 hipError_t dequant_matmul_launch(const DequantArgs &a, hipStream_t st) {
+    if (dequant_wide(a.m, a.a_bf16, a.d_in)) {
+        switch (a.bits) {
+            case 2: return launch_gemm_bits<2>(a, st);
+            case 3: return launch_gemm_bits<3>(a, st);
+            case 4: return launch_gemm_bits<4>(a, st);
+            case 8: return launch_gemm_bits<8>(a, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (a.bits) {
         case 2: return launch_gemv_bits<2>(a, st);
         case 3: return launch_gemv_bits<3>(a, st);

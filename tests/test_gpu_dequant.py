@@ -10,11 +10,13 @@ Tolerances:
     scales, integer zero points, partial sums far below 2^24 units of the
     finest scale): every product and sum is exact in fp32, so Y must equal
     the oracle bit for bit;
-  * otherwise, from the kernel's arithmetic: each 16-code dot product and
-    activation sum is an fp32 sum of 16 terms, folded with two roundings, the
-    folds summed along the work group's k-range, the k-splits summed in
-    order; so |dY| <= 2^-24 (d_in/16 + 100) T with T = sum_k |a_k| s (q_k +
-    z) (the magnitudes the fp32 sums carry), plus half a bf16 step of |Y|
+  * otherwise, from the kernels' arithmetic: on the skinny path each 16-code
+    dot product and activation sum is an fp32 sum of 16 terms, folded with
+    two roundings, the folds summed along the work group's k-range, the
+    k-splits summed in order; on the wide path a group's products are summed
+    in fp32 by the matrix cores and the groups folded in order; so
+    |dY| <= 2^-24 (max(g, 16) + d_in/16 + 100) T with T = sum_k |a_k| s (q_k
+    + z) (the magnitudes the fp32 sums carry), plus half a bf16 step of |Y|
     when Y is bf16.
 """
 import sys
@@ -89,7 +91,9 @@ def bound(A64, codes, scales, zeros, perm, ge, y_ref, y_dtype):
     z = zeros[gi].T.astype(np.float64)
     Ap = np.abs(A64[:, perm])                      # processing order
     T = Ap @ (s * (codes + z)).T
-    b = 2.0 ** -24 * (d_in / 16 + 100) * T
+    # skinny path: 16-term sums folded along k; wide path: a whole group
+    # summed in fp32 by the matrix cores, then the groups folded
+    b = 2.0 ** -24 * (max(ge, 16) + d_in / 16 + 100) * T
     if y_dtype == "bf16":
         b = b + 2.0 ** -8 * np.abs(y_ref)
     return b
@@ -103,6 +107,13 @@ EXACT_CASES = [   # (d_out, d_in, bits, g, m, act_order, a_dtype, seed)
     (640, 96, 8, -1, 2, False, "f32", 5),       # one group per row, 8-bit
     (77, 33, 3, 16, 11, True, "bf16", 6),       # m above one launch, ragged everything
     (4096, 1024, 4, 64, 4, True, "bf16", 7),
+    # the wide (MFMA) path: bf16 activations, m >= 16, d_in % 8 == 0
+    (512, 256, 4, 128, 64, True, "bf16", 21),
+    (300, 1000, 3, 32, 300, True, "bf16", 22),   # ragged row and column tiles, 3-bit straddles
+    (640, 96, 8, -1, 48, False, "bf16", 23),     # one group per row, 8-bit codes up to 255
+    (130, 136, 2, 16, 17, True, "bf16", 24),     # groups of 16 ending inside a 64-code chunk
+    (1024, 4096, 4, 128, 257, False, "bf16", 25),
+    (96, 512, 4, 128, 40, True, "f32", 26),      # fp32 activations stay on the skinny path
 ]
 
 
@@ -127,6 +138,9 @@ ROUND_CASES = [   # (d_out, d_in, bits, g, m, act_order, y_dtype, seed): the lay
     (11008, 4096, 3, 32, 1, True, "f32", 13),     # up_proj
     (4096, 11008, 4, 128, 2, True, "f32", 14),    # down_proj
     (8192, 28672, 4, 128, 1, False, "bf16", 15),  # 70B down_proj
+    (4096, 4096, 4, 128, 512, True, "f32", 16),   # prefill shapes on the wide path
+    (11008, 4096, 3, 32, 128, True, "bf16", 17),
+    (4096, 11008, 4, 128, 64, True, "f32", 18),
 ]
 
 
