@@ -114,6 +114,11 @@ EXACT_CASES = [   # (d_out, d_in, bits, g, m, act_order, a_dtype, seed)
     (130, 136, 2, 16, 17, True, "bf16", 24),     # groups of 16 ending inside a 64-code chunk
     (1024, 4096, 4, 128, 257, False, "bf16", 25),
     (96, 512, 4, 128, 40, True, "f32", 26),      # fp32 activations stay on the skinny path
+    # streamed wide form (d_in % 32 == 0): ring of 32-code stages
+    (300, 992, 3, 32, 300, True, "bf16", 27),    # ragged tiles, 3-bit units straddling words
+    (130, 160, 2, 16, 17, True, "bf16", 28),     # groups of 16, two per stage
+    (257, 64, 8, 16, 20, False, "bf16", 29),     # two stages only: most of the ring issued past the end
+    (200, 480, 4, 48, 33, True, "bf16", 30),     # groups of 48 ending mid-stage
 ]
 
 
