@@ -13,8 +13,10 @@
 // weights once.  A work group owns 256 output rows (four adjacent rows per
 // lane, so a packed word row is one contiguous kilobyte read by a wave as
 // 16-byte loads) and one of `nsplit` ranges of k; k is cut into 32-code units
-// (a unit is `bits` consecutive words of a row) and the group's four waves
-// take every fourth unit of its range.  The group gathers its range of A_p
+// (a unit is `bits` consecutive words of a row) and the group's waves take
+// every fourth (or eighth) unit of its range: eight waves for one activation
+// row on layers under 16 MB of packed words, whose few work groups would
+// otherwise leave half the SIMDs idle, with all of a wave's words in flight.  The group gathers its range of A_p
 // into LDS as fp32, with the sum of every 16 consecutive activations.  Codes
 // are extracted with constant shifts and multiplied with the broadcast
 // activations into a 16-code dot product, folded as
@@ -22,7 +24,7 @@
 // so the group's scale and zero point are applied once per 16 codes and a
 // group may end at any multiple of 16.  The units' packed words, scales and
 // zero points are loaded a few units ahead, the first ones before the
-// activations are staged.  The four waves' sums meet in LDS; the k-ranges'
+// activations are staged.  The waves' sums meet in LDS; the k-ranges'
 // partial sums go to the workspace, and the last work group of a row tile to
 // finish (a device-scope counter per tile, reset by that group) adds them in
 // split order and writes Y as fp32 or bf16: deterministic, one launch.  No
@@ -78,14 +80,16 @@ __device__ __forceinline__ void half_unit_dot(const u32x4 (&w)[BITS], const floa
     (one(std::integral_constant<int, KK>{}), ...);
 }
 
-// units whose packed words are in flight per lane (about 8 words of registers)
-template <int BITS>
+// units whose packed words are in flight per lane: about 16 words of
+// registers for one activation row in eight-wave groups, 8 otherwise
+template <int BITS, int M, int NW>
 constexpr int prefetch_units() {
-    return BITS <= 2 ? 4 : (BITS <= 4 ? 2 : 1);
+    return (M == 1 && NW == 8) ? (BITS <= 2 ? 6 : (BITS <= 4 ? 16 / BITS : 2))
+                               : (BITS <= 2 ? 4 : (BITS <= 4 ? 2 : 1));
 }
 
-template <int BITS, int M, bool VEC, bool G32>
-__global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A, int a_bf16,
+template <int BITS, int M, int NW, bool VEC, bool G32>
+__global__ __launch_bounds__(64 * NW) void dq_gemv_kernel(const void *__restrict__ A, int a_bf16,
                                                       const int32_t *__restrict__ perm,
                                                       const uint32_t *__restrict__ Q,
                                                       const float *__restrict__ scales,
@@ -94,7 +98,8 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
                                                       int32_t *__restrict__ counters, int64_t m_total, int64_t m0,
                                                       int64_t d_in, int64_t d_out, int g, int ngroups, int nunits,
                                                       int nsplit, int64_t nwords) {
-    constexpr int PF = prefetch_units<BITS>();
+    constexpr int PF = prefetch_units<BITS, M, NW>();
+    constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) float a_lds[GV_LDS];
     __shared__ float hs_lds[GV_LDS / 16];
     __shared__ int last_flag;
@@ -156,15 +161,15 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
 #pragma unroll
         for (int i = 0; i < M; ++i) acc[j][i] = 0.f;
 
-    // this wave's units of the range: wave, wave + 4, ...
-    const int nmy = wave < nu ? (nu - 1 - wave) / 4 + 1 : 0;
+    // this wave's units of the range: wave, wave + NW, ...
+    const int nmy = wave < nu ? (nu - 1 - wave) / NW + 1 : 0;
     Slot sl[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-        if (p < nmy) fetch(u0 + wave + 4 * p, sl[p]);
+        if (p < nmy) fetch(u0 + wave + NW * p, sl[p]);
     // stage A_p for the range (rows past m_total read 0)
     const int64_t k0 = (int64_t)u0 * UNIT;
-    for (int idx = tid; idx < M * kw; idx += 256) {
+    for (int idx = tid; idx < M * kw; idx += NT) {
         const int i = idx / kw, kk = idx - i * kw;
         const int64_t k = k0 + kk, row = m0 + i;
         float v = 0.f;
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
         a_lds[i * kw + kk] = v;
     }
     __syncthreads();
-    for (int idx = tid; idx < M * 2 * nu; idx += 256) {
+    for (int idx = tid; idx < M * 2 * nu; idx += NT) {
         const int i = idx / (2 * nu), h = idx - i * 2 * nu;
         const float *p = a_lds + i * kw + 16 * h;
         float s = 0.f;
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
         for (int p = 0; p < PF; ++p) {
             const int it = i0 + p;
             if (it < nmy) {
-                const int ul = wave + 4 * it;          // unit within the range
+                const int ul = wave + NW * it;         // unit within the range
                 const float *al = a_lds + ul * UNIT;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -213,12 +218,12 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
                         for (int i = 0; i < M; ++i) acc[j][i] = fmaf(sj, dot[j][i], fmaf(-szj, hs[i], acc[j][i]));
                     }
                 }
-                if (it + PF < nmy) fetch(u0 + wave + 4 * (it + PF), sl[p]);
+                if (it + PF < nmy) fetch(u0 + wave + NW * (it + PF), sl[p]);
             }
         }
     }
 
-    // the four waves' sums, added in wave order: red[wave][row][i]
+    // the waves' sums, added in wave order: red[wave][row][i]
     __syncthreads();
     float *red = a_lds;
 #pragma unroll
@@ -226,14 +231,16 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
 #pragma unroll
         for (int i = 0; i < M; ++i) red[(wave * GV_ROWS + 4 * lane + j) * M + i] = acc[j][i];
     __syncthreads();
-    // thread t: row t of the tile, all M activation rows
+    // thread t < 256: row t of the tile, all M activation rows
+    const bool row_thread = tid < GV_ROWS;
     const int64_t r = (int64_t)blockIdx.x * GV_ROWS + tid;
     float mine[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         float v = 0.f;
+        if (row_thread)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) v += red[(w * GV_ROWS + tid) * M + i];
+            for (int w = 0; w < NW; ++w) v += red[(w * GV_ROWS + tid) * M + i];
         mine[i] = v;
     }
     auto store_y = [&](int i, float v) {
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
         }
     };
     if (nsplit == 1) {
-        if (r < d_out)
+        if (row_thread && r < d_out)
 #pragma unroll
             for (int i = 0; i < M; ++i)
                 if (m0 + i < m_total) store_y(i, mine[i]);
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
     // reads every partial.  This is the ordering a device-scope release and
     // acquire give, without writing back and invalidating the whole L2 in
     // every group (which made the product three times slower).
-    if (r < d_out)
+    if (row_thread && r < d_out)
 #pragma unroll
         for (int i = 0; i < M; ++i)
             __hip_atomic_store(&part[((int64_t)split * M + i) * d_out + r], mine[i], __ATOMIC_RELAXED,
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
     }
     __syncthreads();
     if (!last_flag) return;
-    if (r < d_out) {
+    if (row_thread && r < d_out) {
 #pragma unroll
         for (int i = 0; i < M; ++i) {
             // split order, eight loads in flight at a time
@@ -298,6 +305,14 @@ __global__ __launch_bounds__(256) void dq_gemv_kernel(const void *__restrict__ A
     if (tid == 0) counters[blockIdx.x] = 0;    // ready for the next call on this workspace
 }
 
+// waves per work group: eight for one activation row on layers under 16 MB
+// of packed words (few work groups there, so every SIMD gets a share), four
+// otherwise (the streaming shapes and the wider accumulators)
+int gemv_waves(int M, int64_t d_out, int64_t d_in, int bits) {
+    const int64_t packed = d_out * cdiv((int64_t)bits * d_in, 32) * 4;
+    return (M == 1 && packed < ((int64_t)16 << 20)) ? 8 : 4;
+}
+
 // work groups along k for a launch of M activation rows: about 128 work
 // groups in all for layers under 16 MB of packed words (fixed costs per group
 // dominate there) and 512 above, each wave with at least one unit, the staged
@@ -309,7 +324,7 @@ int gemv_splits(int M, int64_t d_out, int64_t d_in, int bits) {
     const int64_t packed = d_out * cdiv((int64_t)bits * d_in, 32) * 4;
     const int64_t target = packed < ((int64_t)16 << 20) ? 128 : 512;
     int64_t s = std::max<int64_t>(1, target / tiles);
-    s = std::min<int64_t>(s, std::max(1, nunits / 4));
+    s = std::min<int64_t>(s, std::max(1, nunits / gemv_waves(M, d_out, d_in, bits)));
     s = std::max<int64_t>(s, cdiv(nunits, max_units));
     return (int)s;
 }
@@ -322,7 +337,15 @@ void launch_gemv_k(const DequantArgs &a, int64_t m0, hipStream_t st) {
     const dim3 grid((unsigned)cdiv(a.d_out, GV_ROWS), (unsigned)nsplit);
     const int nunits = (int)cdiv(a.d_in, UNIT);
     const int64_t nwords = cdiv((int64_t)BITS * a.d_in, 32);
-    dq_gemv_kernel<BITS, M, VEC, G32><<<grid, 256, 0, st>>>(a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y,
+    if constexpr (M == 1) {
+        if (gemv_waves(M, a.d_out, a.d_in, BITS) == 8) {
+            dq_gemv_kernel<BITS, M, 8, VEC, G32><<<grid, 512, 0, st>>>(
+                a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.part, a.counters, a.m, m0, a.d_in,
+                a.d_out, a.group, a.ngroups, nunits, nsplit, nwords);
+            return;
+        }
+    }
+    dq_gemv_kernel<BITS, M, 4, VEC, G32><<<grid, 256, 0, st>>>(a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y,
                                                             a.y_bf16, a.part, a.counters, a.m, m0, a.d_in, a.d_out,
                                                             a.group, a.ngroups, nunits, nsplit, nwords);
 }
@@ -552,9 +575,9 @@ __global__ __launch_bounds__(512) void dq_gemm_kernel(const uint16_t *__restrict
 // in the same branch-free block so that the conversions fill the issue slots
 // between the matrix instructions, and further stages are in flight.  One
 // barrier per stage.  A work group of NW waves (NW / 2 x 2, each 64 x 64 of
-// Y) owns 32 NW x 128 of Y.  With four waves (128 x 128, about 76 KB of LDS)
-// two work groups share a compute unit and run independently, so the
-// barrier and latency bubbles of one are filled by the other's products.
+// Y) owns 32 NW x 128 of Y; launches use eight (256 x 128, one group per
+// CU): four-wave groups of 128 x 128, two per CU, were slower, the per-stage
+// costs being per group.
 // Activation pieces are swizzled within their 64-byte LDS row so that the
 // 16-byte operand reads of 8 or 16 consecutive rows fall on distinct banks.
 // Waves with no packed-word load of their own in a stage issue a dummy one,
