@@ -19,7 +19,8 @@
 // otherwise leave half the SIMDs idle, with all of a wave's words in flight.  The group gathers its range of A_p
 // into LDS as fp32, with the sum of every 16 consecutive activations.  Codes
 // are extracted with constant shifts and multiplied with the broadcast
-// activations into a 16-code dot product, folded as
+// activations into a 16-code dot product (two or more bf16 activation rows:
+// code pairs as exact bf16 pairs through v_dot2c_f32_bf16), folded as
 //   acc += s dot - (s z) sum16(A_p),
 // so the group's scale and zero point are applied once per 16 codes and a
 // group may end at any multiple of 16.  The units' packed words, scales and
@@ -80,6 +81,31 @@ __device__ __forceinline__ void half_unit_dot(const u32x4 (&w)[BITS], const floa
     (one(std::integral_constant<int, KK>{}), ...);
 }
 
+// The same sums for bf16 activations (staged as bf16 pairs, a2[i][k / 2]):
+// codes k, k+1 become an exact bf16 pair and one v_dot2c_f32_bf16 adds both
+// products per activation row
+typedef __attribute__((ext_vector_type(2))) __bf16 gv_bf16x2;
+template <int BITS, int M, int H, int... PP>
+__device__ __forceinline__ void half_unit_dot2(const u32x4 (&w)[BITS], const unsigned *a2, int astride2,
+                                               float (&dot)[4][M], std::integer_sequence<int, PP...>) {
+    auto one = [&](auto pc) {
+        constexpr int k = 2 * decltype(pc)::value + 16 * H;
+        gv_bf16x2 a[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) a[i] = __builtin_bit_cast(gv_bf16x2, a2[i * astride2 + k / 2]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            unsigned wj[BITS];
+#pragma unroll
+            for (int b = 0; b < BITS; ++b) wj[b] = w[b][j];
+            const gv_bf16x2 q = {(__bf16)(float)unit_code<BITS, k>(wj), (__bf16)(float)unit_code<BITS, k + 1>(wj)};
+#pragma unroll
+            for (int i = 0; i < M; ++i) dot[j][i] = __builtin_amdgcn_fdot2_f32_bf16(a[i], q, dot[j][i], false);
+        }
+    };
+    (one(std::integral_constant<int, PP>{}), ...);
+}
+
 // units whose packed words are in flight per lane: about 16 words of
 // registers for one activation row in eight-wave groups, 8 otherwise
 template <int BITS, int M, int NW>
@@ -88,7 +114,8 @@ constexpr int prefetch_units() {
                                : (BITS <= 2 ? 4 : (BITS <= 4 ? 2 : 1));
 }
 
-template <int BITS, int M, int NW, bool VEC, bool G32>
+// D2: bf16 activations summed in pairs by v_dot2c_f32_bf16 (staged as bf16)
+template <int BITS, int M, int NW, bool VEC, bool G32, bool D2>
 __global__ __launch_bounds__(64 * NW) void dq_gemv_kernel(const void *__restrict__ A, int a_bf16,
                                                       const int32_t *__restrict__ perm,
                                                       const uint32_t *__restrict__ Q,
@@ -167,25 +194,40 @@ __global__ __launch_bounds__(64 * NW) void dq_gemv_kernel(const void *__restrict
 #pragma unroll
     for (int p = 0; p < PF; ++p)
         if (p < nmy) fetch(u0 + wave + NW * p, sl[p]);
-    // stage A_p for the range (rows past m_total read 0)
+    // stage A_p for the range (rows past m_total read 0): fp32, or the bf16
+    // values themselves for D2
     const int64_t k0 = (int64_t)u0 * UNIT;
+    uint16_t *a16 = (uint16_t *)a_lds;
     for (int idx = tid; idx < M * kw; idx += NT) {
         const int i = idx / kw, kk = idx - i * kw;
         const int64_t k = k0 + kk, row = m0 + i;
-        float v = 0.f;
-        if (k < d_in && row < m_total) {
-            const int64_t c = perm ? (int64_t)perm[k] : k;
-            v = a_bf16 ? bf16_bits_to_f32(((const uint16_t *)A)[row * d_in + c]) : ((const float *)A)[row * d_in + c];
+        if (D2) {
+            uint16_t v = 0;
+            if (k < d_in && row < m_total) v = ((const uint16_t *)A)[row * d_in + (perm ? (int64_t)perm[k] : k)];
+            a16[i * kw + kk] = v;
+        } else {
+            float v = 0.f;
+            if (k < d_in && row < m_total) {
+                const int64_t c = perm ? (int64_t)perm[k] : k;
+                v = a_bf16 ? bf16_bits_to_f32(((const uint16_t *)A)[row * d_in + c])
+                           : ((const float *)A)[row * d_in + c];
+            }
+            a_lds[i * kw + kk] = v;
         }
-        a_lds[i * kw + kk] = v;
     }
     __syncthreads();
     for (int idx = tid; idx < M * 2 * nu; idx += NT) {
         const int i = idx / (2 * nu), h = idx - i * 2 * nu;
-        const float *p = a_lds + i * kw + 16 * h;
         float s = 0.f;
+        if (D2) {
+            const uint16_t *p = a16 + i * kw + 16 * h;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) s += p[t];
+            for (int t = 0; t < 16; ++t) s += bf16_bits_to_f32(p[t]);
+        } else {
+            const float *p = a_lds + i * kw + 16 * h;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) s += p[t];
+        }
         hs_lds[i * 2 * nu + h] = s;
     }
     __syncthreads();
@@ -196,6 +238,7 @@ __global__ __launch_bounds__(64 * NW) void dq_gemv_kernel(const void *__restrict
             if (it < nmy) {
                 const int ul = wave + NW * it;         // unit within the range
                 const float *al = a_lds + ul * UNIT;
+                const unsigned *al2 = (const unsigned *)(a16 + ul * UNIT);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     float hs[M];
@@ -206,10 +249,17 @@ __global__ __launch_bounds__(64 * NW) void dq_gemv_kernel(const void *__restrict
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
                         for (int i = 0; i < M; ++i) dot[j][i] = 0.f;
-                    if (h == 0)
-                        half_unit_dot<BITS, M, 0>(sl[p].w, al, kw, dot, std::make_integer_sequence<int, 16>{});
-                    else
-                        half_unit_dot<BITS, M, 1>(sl[p].w, al, kw, dot, std::make_integer_sequence<int, 16>{});
+                    if (D2) {
+                        if (h == 0)
+                            half_unit_dot2<BITS, M, 0>(sl[p].w, al2, kw / 2, dot, std::make_integer_sequence<int, 8>{});
+                        else
+                            half_unit_dot2<BITS, M, 1>(sl[p].w, al2, kw / 2, dot, std::make_integer_sequence<int, 8>{});
+                    } else {
+                        if (h == 0)
+                            half_unit_dot<BITS, M, 0>(sl[p].w, al, kw, dot, std::make_integer_sequence<int, 16>{});
+                        else
+                            half_unit_dot<BITS, M, 1>(sl[p].w, al, kw, dot, std::make_integer_sequence<int, 16>{});
+                    }
                     const int hh = G32 ? 0 : h;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -331,7 +381,7 @@ int gemv_splits(int M, int64_t d_out, int64_t d_in, int bits) {
 
 int pad_m(int64_t mc) { return mc <= 1 ? 1 : (mc <= 2 ? 2 : (mc <= 4 ? 4 : 8)); }
 
-template <int BITS, int M, bool VEC, bool G32>
+template <int BITS, int M, bool VEC, bool G32, bool D2>
 void launch_gemv_k(const DequantArgs &a, int64_t m0, hipStream_t st) {
     const int nsplit = gemv_splits(M, a.d_out, a.d_in, BITS);
     const dim3 grid((unsigned)cdiv(a.d_out, GV_ROWS), (unsigned)nsplit);
@@ -339,30 +389,39 @@ void launch_gemv_k(const DequantArgs &a, int64_t m0, hipStream_t st) {
     const int64_t nwords = cdiv((int64_t)BITS * a.d_in, 32);
     if constexpr (M == 1) {
         if (gemv_waves(M, a.d_out, a.d_in, BITS) == 8) {
-            dq_gemv_kernel<BITS, M, 8, VEC, G32><<<grid, 512, 0, st>>>(
+            dq_gemv_kernel<BITS, M, 8, VEC, G32, D2><<<grid, 512, 0, st>>>(
                 a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.part, a.counters, a.m, m0, a.d_in,
                 a.d_out, a.group, a.ngroups, nunits, nsplit, nwords);
             return;
         }
     }
-    dq_gemv_kernel<BITS, M, 4, VEC, G32><<<grid, 256, 0, st>>>(a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y,
+    dq_gemv_kernel<BITS, M, 4, VEC, G32, D2><<<grid, 256, 0, st>>>(a.A, a.a_bf16, a.perm, a.Q, a.scales, a.zeros, a.Y,
                                                             a.y_bf16, a.part, a.counters, a.m, m0, a.d_in, a.d_out,
                                                             a.group, a.ngroups, nunits, nsplit, nwords);
 }
 
-template <int BITS, int M>
-hipError_t launch_gemv_m(const DequantArgs &a, int64_t m0, hipStream_t st) {
+template <int BITS, int M, bool D2>
+hipError_t launch_gemv_md(const DequantArgs &a, int64_t m0, hipStream_t st) {
     const bool vec = a.d_out % 4 == 0;
     const bool g32 = a.group % 32 == 0 || a.ngroups == 1;
     if (vec && g32)
-        launch_gemv_k<BITS, M, true, true>(a, m0, st);
+        launch_gemv_k<BITS, M, true, true, D2>(a, m0, st);
     else if (vec)
-        launch_gemv_k<BITS, M, true, false>(a, m0, st);
+        launch_gemv_k<BITS, M, true, false, D2>(a, m0, st);
     else if (g32)
-        launch_gemv_k<BITS, M, false, true>(a, m0, st);
+        launch_gemv_k<BITS, M, false, true, D2>(a, m0, st);
     else
-        launch_gemv_k<BITS, M, false, false>(a, m0, st);
+        launch_gemv_k<BITS, M, false, false, D2>(a, m0, st);
     return hipGetLastError();
+}
+
+// bf16 activations in launches of two or more rows take the pairwise dot
+template <int BITS, int M>
+hipError_t launch_gemv_m(const DequantArgs &a, int64_t m0, hipStream_t st) {
+    if constexpr (M >= 2) {
+        if (a.a_bf16) return launch_gemv_md<BITS, M, true>(a, m0, st);
+    }
+    return launch_gemv_md<BITS, M, false>(a, m0, st);
 }
 
 template <int BITS>
