@@ -625,45 +625,48 @@ __global__ __launch_bounds__(512) void dq_gemm_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// Wide path, streamed form (d_in % 32 == 0).  The same product, but k moves
-// in stages of 32 (one 32-code unit) through an LDS ring that buffer loads
-// fill directly (no register round trip): per stage the activations
-// (16-byte pieces), the unit's packed words and the scales and zero points of
-// the stage's two 16-code halves.  While the products of stage c run, stage
-// c+1's codes are dequantized (q - z, bf16) into one of two LDS weight tiles,
-// in the same branch-free block so that the conversions fill the issue slots
-// between the matrix instructions, and further stages are in flight.  One
-// barrier per stage.  A work group of NW waves (NW / 2 x 2, each 64 x 64 of
-// Y) owns 32 NW x 128 of Y; launches use eight (256 x 128, one group per
-// CU): four-wave groups of 128 x 128, two per CU, were slower, the per-stage
-// costs being per group.
-// Activation pieces are swizzled within their 64-byte LDS row so that the
-// 16-byte operand reads of 8 or 16 consecutive rows fall on distinct banks.
-// Waves with no packed-word load of their own in a stage issue a dummy one,
-// so that every wave counts the same loads per stage.
+// Wide path, streamed form (d_in a multiple of the stage width KC).  The same
+// product and the same 256 x 128 tiles of Y (8 waves, 4 x 2, each 64 x 64),
+// but k moves in stages of KC (32 or 64 codes, one or two units) through an
+// LDS ring that buffer loads fill directly (no register round trip): per
+// stage the unit's packed words, the scales and zero points of its 16-code
+// halves, then the activations (256 x KC bf16, 16-byte pieces).  While the
+// products of stage c run, stage c+1's codes are dequantized (q - z, bf16)
+// into one of two LDS weight tiles, in the same branch-free block, so that
+// the conversions fill the issue slots between the matrix instructions.  One
+// barrier per stage; at its end a wave waits only until the next stage's
+// codes have landed, so the activations (issued last) have two stages to
+// arrive.  Stages of 64 (codes of up to 4 bits) halve the barriers and
+// per-stage costs per product; 8-bit codes take stages of 32 (a 64-wide
+// ring would not fit the LDS).  Activation pieces are swizzled within their
+// LDS row so that the 16-byte operand reads of 8 or 16 consecutive rows fall
+// on distinct banks.  Waves with no packed-word load of their own in a stage
+// issue a dummy one, so that every wave counts the same loads per stage.
 // ---------------------------------------------------------------------------
-constexpr int GR_KC = 32;              // k per stage (one unit)
-constexpr int GR_WAVES = 8;            // waves per work group (256 x 128 tiles of Y)
-constexpr int GR_BROW = GR_KC + 8;     // bf16 per staged weight row (padding)
+constexpr int GR_NW = 8;   // waves per work group
 
-template <int BITS, int NW>
+template <int BITS, int KC>
 struct GrLayout {
-    static constexpr int BM = 32 * NW;                   // activation rows of the tile
-    static constexpr int NST = NW == 8 ? 6 : 4;          // ring stages
-    static constexpr int A_STAGE = BM * GR_KC * 2;       // activation bytes per stage
-    static constexpr int Q_STAGE = BITS * GM_BN * 4;     // packed words per stage
-    static constexpr int SZ_STAGE = 4 * GM_BN * 4;       // [s, z][half][128] floats
+    static constexpr int KS = KC / 16;                    // k steps of 16 per stage
+    static constexpr int UPS = KC / 32;                   // 32-code units per stage
+    static constexpr int NST = KC == 32 ? 6 : 3;          // ring stages
+    static constexpr int AROW = KC * 2;                   // bytes of one activation row per stage
+    static constexpr int A_STAGE = GM_BM * AROW;
+    static constexpr int BROW = KC + 8;                   // bf16 per staged weight row (padding)
+    static constexpr int Q_STAGE = UPS * BITS * GM_BN * 4;
+    static constexpr int SZ_STAGE = 2 * KS * GM_BN * 4;   // [s, z][half][128] floats
     static constexpr int Q_OFF = NST * A_STAGE;
     static constexpr int SZ_OFF = Q_OFF + NST * Q_STAGE;
     static constexpr int B_OFF = SZ_OFF + NST * SZ_STAGE;
-    static constexpr int B_BUF = GM_BN * GR_BROW * 2;
-    static constexpr int JUNK_OFF = B_OFF + 2 * B_BUF;   // target of the dummy loads
+    static constexpr int B_BUF = GM_BN * BROW * 2;
+    static constexpr int JUNK_OFF = B_OFF + 2 * B_BUF;    // target of the dummy loads
     static constexpr int BYTES = JUNK_OFF + 256;
-    static constexpr int ADMA = BM / 16 / NW;            // activation loads per wave and stage (1 KB each)
-    static constexpr int QDMA = (2 * BITS + NW - 1) / NW;   // packed-word loads per wave and stage (256 B)
-    static constexpr int SDMA = 8 / NW;                  // scale / zero-point loads per wave and stage
-    static constexpr int PER_STAGE = ADMA + QDMA + SDMA; // loads per wave and stage
-    static constexpr int CPT = 2 * GR_KC / NW;           // codes each thread dequantizes per stage
+    static constexpr int ADMA = A_STAGE / 1024 / GR_NW;   // activation loads per wave and stage (1 KB)
+    static constexpr int QDMA = (2 * BITS * UPS + GR_NW - 1) / GR_NW;   // packed-word loads (256 B)
+    static constexpr int SDMA = 4 * KS / GR_NW;           // scale / zero-point loads (256 B)
+    static constexpr int PER_STAGE = ADMA + QDMA + SDMA;
+    static constexpr int NCH = GM_BN * KC / (64 * GR_NW) / 8;   // 8-code chunks each thread dequantizes
+    static_assert(BYTES <= 160 * 1024, "the ring fits the LDS");
 };
 
 typedef __attribute__((address_space(3))) void gr_lds_void_t;
@@ -688,123 +691,133 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gr_rsrc(const void *p, int64_t
     return __builtin_amdgcn_make_buffer_rsrc((void *)bu, (short)0, n, 0x00020000);
 }
 
-// 16-byte piece position of an activation row inside its 64-byte LDS row
-__device__ __forceinline__ int gr_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// 16-byte piece position of an activation row inside its LDS row: four
+// pieces (stages of 32) or eight (stages of 64)
+template <int KC>
+__device__ __forceinline__ int gr_swz(int row) {
+    if constexpr (KC == 32)
+        return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+    else
+        return ((row >> 1) ^ ((row & 1) << 2)) & 7;
+}
 
-template <int BITS, int NW>
-__global__ __launch_bounds__(64 * NW) void dq_gemm_ring_kernel(const uint16_t *__restrict__ A,
-                                                               const uint32_t *__restrict__ Q,
-                                                               const float *__restrict__ scales,
-                                                               const float *__restrict__ zeros,
-                                                               void *__restrict__ Y, int y_bf16, int64_t m,
-                                                               int64_t d_in, int64_t d_out, int g, int ngroups,
-                                                               int64_t nwords) {
-    using L = GrLayout<BITS, NW>;
+template <int BITS, int KC>
+__global__ __launch_bounds__(64 * GR_NW) void dq_gemm_ring_kernel(const uint16_t *__restrict__ A,
+                                                                  const uint32_t *__restrict__ Q,
+                                                                  const float *__restrict__ scales,
+                                                                  const float *__restrict__ zeros,
+                                                                  void *__restrict__ Y, int y_bf16, int64_t m,
+                                                                  int64_t d_in, int64_t d_out, int g, int ngroups,
+                                                                  int64_t nwords) {
+    using L = GrLayout<BITS, KC>;
     // (arrays that the lambdas below capture have literal sizes, their
     // largest counts: with value-dependent sizes the host pass drops the
     // kernel's launch stub)
-    constexpr int NST = L::NST, ADMA = L::ADMA, QDMA = L::QDMA, SDMA = L::SDMA;
-    static_assert(ADMA <= 2 && QDMA <= 4 && SDMA <= 2 && L::CPT / 8 <= 2, "per-thread array bounds");
+    constexpr int NST = L::NST, KS = L::KS, ADMA = L::ADMA, QDMA = L::QDMA, SDMA = L::SDMA, NCH = L::NCH;
+    static_assert(ADMA <= 4 && QDMA <= 2 && SDMA <= 2 && NCH <= 2, "per-thread array bounds");
+    constexpr int RPI = 1024 / L::AROW, PPR = L::AROW / 16;   // activation rows per load, pieces per row
     __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.x * L::BM, n0 = (int64_t)blockIdx.y * GM_BN;
-    const int nst = (int)(d_in / GR_KC);
+    const int64_t m0 = (int64_t)blockIdx.x * GM_BM, n0 = (int64_t)blockIdx.y * GM_BN;
+    const int nst = (int)(d_in / KC);
 
     // Every load address is clamped into its operand (rows past m re-read
     // the last row, columns past d_out the last column, stages past the end
     // the last stage: all only feed entries that are never stored), so no
     // load relies on buffer range checks; per-lane offsets are fixed and the
     // stage moves only the scalar offset.
-    const int rows = (int)(std::min<int64_t>(m, m0 + L::BM) - m0);
+    const int rows = (int)(std::min<int64_t>(m, m0 + GM_BM) - m0);
     const int cols = (int)(std::min<int64_t>(d_out, n0 + GM_BN) - n0);
     const __amdgpu_buffer_rsrc_t arsrc = gr_rsrc(A + m0 * d_in, (int64_t)rows * d_in * 2);
     const __amdgpu_buffer_rsrc_t qrsrc = gr_rsrc(Q + n0, (nwords * d_out - n0) * 4);
     const __amdgpu_buffer_rsrc_t srsrc = gr_rsrc(scales + n0, ((int64_t)ngroups * d_out - n0) * 4);
     const __amdgpu_buffer_rsrc_t zrsrc = gr_rsrc(zeros + n0, ((int64_t)ngroups * d_out - n0) * 4);
-    // activation load j = ADMA wave + q of a stage fills LDS rows 16 j ..
-    // 16 j + 15; lane l lands in row 16 j + l / 4 at piece position l % 4,
-    // holding the piece that the swizzle places there
-    int aoff[2];
+    // activation load j = ADMA wave + q of a stage fills LDS rows RPI j ..
+    // RPI j + RPI - 1; lane l lands in row RPI j + l / PPR at piece position
+    // l % PPR, holding the piece that the swizzle places there
+    int aoff[4];
 #pragma unroll
     for (int q = 0; q < ADMA; ++q) {
-        const int r = 16 * (ADMA * wave + q) + (lane >> 2);
-        const int p = (lane & 3) ^ gr_swz(r);
+        const int r = RPI * (ADMA * wave + q) + lane / PPR;
+        const int p = (lane % PPR) ^ gr_swz<KC>(r);
         aoff[q] = std::min(r, rows - 1) * (int)d_in * 2 + 16 * p;
     }
-    // packed-word load i = wave + NW t: word row i / 2 of the unit, columns
-    // 64 (i % 2) .. +63 (a dummy re-read of row 0 when i >= 2 bits)
-    int qoff[4];
+    // packed-word load i = wave + 8 t: word row i / 2 of the stage, columns
+    // 64 (i % 2) .. +63 (a dummy re-read of row 0 when i >= 2 bits units)
+    int qoff[2];
 #pragma unroll
     for (int t = 0; t < QDMA; ++t) {
-        const int i = wave + NW * t;
-        qoff[t] = i < 2 * BITS ? ((i >> 1) * (int)d_out + std::min(64 * (i & 1) + lane, cols - 1)) * 4
-                               : std::min(lane, cols - 1) * 4;
+        const int i = wave + GR_NW * t;
+        qoff[t] = i < 2 * BITS * L::UPS ? ((i >> 1) * (int)d_out + std::min(64 * (i & 1) + lane, cols - 1)) * 4
+                                        : std::min(lane, cols - 1) * 4;
     }
-    // scale / zero-point load i = wave + NW t: tensor i / 4 (s, z), half
-    // i / 2 % 2 of the stage, columns 64 (i % 2) .. +63
+    // scale / zero-point load i = wave + 8 t: tensor i / (2 KS) (s, z), half
+    // i / 2 % KS of the stage, columns 64 (i % 2) .. +63
     int szoff[2];
 #pragma unroll
-    for (int t = 0; t < SDMA; ++t) szoff[t] = std::min(64 * ((wave + NW * t) & 1) + lane, cols - 1) * 4;
-    const int gsteps = g / 16;   // k steps of 16 per group (g is 16, a multiple of 32 or d_in)
-    const int qstride = BITS * (int)d_out * 4, gstride = (int)d_out * 4;
-    // issue tracker: the stage to issue (clamped when loaded) and the group
-    // of its first k step, with that step's place in the group
+    for (int t = 0; t < SDMA; ++t) szoff[t] = std::min(64 * ((wave + GR_NW * t) & 1) + lane, cols - 1) * 4;
+    // k steps of 16 per group: 1, 2 or a multiple of KS (16, 32, whole
+    // stages or one group per row)
+    const int gsteps = g / 16;
+    const int qstride = L::UPS * BITS * (int)d_out * 4, gstride = (int)d_out * 4;
+    // issue tracker: the stage to issue (clamped when loaded), the group of
+    // its first k step and that step's place in the group
     int iss_st = 0, iss_g = 0, iss_r = 0;
 
     auto issue = [&](int slot) {
         const int st = std::min(iss_st, nst - 1);
-        char *base = lds + slot * L::A_STAGE;
-#pragma unroll
-        for (int q = 0; q < ADMA; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (gr_lds_void_t *)(base + (ADMA * wave + q) * 1024),
-                                                     16, aoff[q], st * GR_KC * 2, 0, 0);
+        // packed words and scales first: the next stage's conversions need
+        // them one stage before its products need the activations
         char *qbase = lds + L::Q_OFF + slot * L::Q_STAGE;
         const int qsoff = __builtin_amdgcn_readfirstlane(st * qstride);
 #pragma unroll
         for (int t = 0; t < QDMA; ++t) {
-            const int i = wave + NW * t;
-            gr_lds_void_t *dst = (gr_lds_void_t *)(i < 2 * BITS ? qbase + (i >> 1) * 512 + (i & 1) * 256
-                                                                : lds + L::JUNK_OFF);
+            const int i = wave + GR_NW * t;
+            gr_lds_void_t *dst = (gr_lds_void_t *)(i < 2 * BITS * L::UPS ? qbase + (i >> 1) * 512 + (i & 1) * 256
+                                                                         : lds + L::JUNK_OFF);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, dst, 4, qoff[t], qsoff, 0, 0);
         }
-        // groups of the stage's two halves (scalar offsets: kept uniform so
-        // that no load needs a loop over distinct lane values)
-        const int g0 = std::min(iss_g, ngroups - 1);
-        const int g1 = std::min(iss_g + (iss_r + 1 >= gsteps ? 1 : 0), ngroups - 1);
 #pragma unroll
         for (int t = 0; t < SDMA; ++t) {
-            const int i = wave + NW * t, h = (i >> 1) & 1;
-            const int soff = __builtin_amdgcn_readfirstlane((h ? g1 : g0) * gstride);
+            const int i = wave + GR_NW * t, ten = i / (2 * KS), h = (i >> 1) % KS;
+            // the half's group (g of 16: one per half; of 32: one per two
+            // halves, the stage starting a group; otherwise one per stage)
+            const int gh = iss_g + (gsteps == 1 ? h : (gsteps == 2 ? (h >> 1) : 0));
+            const int soff = __builtin_amdgcn_readfirstlane(std::min(gh, ngroups - 1) * gstride);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                i >> 2 ? zrsrc : srsrc,
-                (gr_lds_void_t *)(lds + L::SZ_OFF + slot * L::SZ_STAGE + ((i >> 2) * 2 + h) * GM_BN * 4 + (i & 1) * 256),
+                ten ? zrsrc : srsrc,
+                (gr_lds_void_t *)(lds + L::SZ_OFF + slot * L::SZ_STAGE + (ten * KS + h) * GM_BN * 4 + (i & 1) * 256),
                 4, szoff[t], soff, 0, 0);
         }
+        char *base = lds + slot * L::A_STAGE;
+#pragma unroll
+        for (int q = 0; q < ADMA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (gr_lds_void_t *)(base + (ADMA * wave + q) * 1024), 16,
+                                                     aoff[q], st * KC * 2, 0, 0);
         ++iss_st;
-        iss_r += 2;
+        iss_r += KS;
         while (iss_r >= gsteps) {
             iss_r -= gsteps;
             ++iss_g;
         }
     };
 
-    // dequantization: thread t turns codes CPT (t / 128) .. +CPT-1 of a
-    // stage's unit in tile row t % 128 into q - z (bf16), eight at a time
+    // dequantization: thread t turns codes 8 (NCH (t / 128) + j) .. +7 of a
+    // stage (j < NCH) in tile row t % 128 into q - z (bf16)
     const int bn = tid & (GM_BN - 1), bpart = tid >> 7;
-    constexpr int NCH = L::CPT / 8;
     int dq_w0[2], dq_w1[2], dq_sh[2];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-        const int cpos = BITS * 8 * (NCH * bpart + j), cj0 = cpos >> 5;
-        dq_w0[j] = L::Q_OFF + (cj0 * GM_BN + bn) * 4;
-        dq_w1[j] = L::Q_OFF + (std::min(cj0 + 1, BITS - 1) * GM_BN + bn) * 4;
+        const int q8 = NCH * bpart + j, uo = q8 >> 2, cpos = BITS * 8 * (q8 & 3), cj0 = cpos >> 5;
+        dq_w0[j] = L::Q_OFF + ((uo * BITS + cj0) * GM_BN + bn) * 4;
+        dq_w1[j] = L::Q_OFF + ((uo * BITS + std::min(cj0 + 1, BITS - 1)) * GM_BN + bn) * 4;
         dq_sh[j] = cpos & 31;
     }
-    // every chunk of a thread lies in one 16-code half
-    const int dq_z = L::SZ_OFF + ((2 + (NCH * bpart) / 2) * GM_BN + bn) * 4;
-    const int dq_dst = L::B_OFF + bn * GR_BROW * 2 + 16 * NCH * bpart;
+    // a thread's chunks lie in one 16-code half
+    const int dq_z = L::SZ_OFF + ((KS + (NCH * bpart) / 2) * GM_BN + bn) * 4;
+    const int dq_dst = L::B_OFF + bn * L::BROW * 2 + 16 * NCH * bpart;
     auto dq_convert = [&](unsigned lo, unsigned hi, int sh, float z) {
         const uint64_t w = (((uint64_t)hi << 32) | (uint64_t)lo) >> sh;
         unsigned pk[4];
@@ -841,104 +854,100 @@ __global__ __launch_bounds__(64 * NW) void dq_gemm_ring_kernel(const uint16_t *_
         }
     // operand reads: lane l supplies row / column l % 32, k 8 (l / 32) .. +7
     const int orow = lane & 31, oh = lane >> 5;
-    const int aswz = gr_swz(orow);   // rows of a lane differ by multiples of 32
-    const int op_a = (wm * 64 + orow) * 64, op_b = L::B_OFF + (wn * 64 + orow) * GR_BROW * 2;
+    const int aswz = gr_swz<KC>(orow);   // rows of a lane differ by multiples of 32
+    const int op_a = (wm * 64 + orow) * L::AROW, op_b = L::B_OFF + (wn * 64 + orow) * L::BROW * 2;
     const int op_s = L::SZ_OFF + (wn * 64 + orow) * 4;
 
     // One stage: the products of stage st (slot `slot`, weight tile st % 2)
-    // and the dequantization of stage st + 1 (slot `nslot`, the other weight
-    // tile).  Group structure of the stage's two k steps, fixed at compile
-    // time: F0 (step 0 starts a group), MID (step 0 ends a group and step 1
-    // starts one), E1 (step 1 ends a group); a starting step begins D from
-    // zero, an ending one adds s D to Y.
-    auto stage = [&](auto f0c, auto midc, auto e1c, int st, int slot, int nslot) {
-        constexpr bool F0 = decltype(f0c)::value, MID = decltype(midc)::value, E1 = decltype(e1c)::value;
+    // and the dequantization of stage st + 1 (slot `nslot`, the other
+    // tile).  Group structure of the stage's KS k steps, fixed at compile
+    // time: bit s of FR, a group starts at step s (D begins from zero); bit
+    // s of EN, a group ends after step s (Y += s D).
+    auto stage = [&](auto frc, auto enc, int st, int slot, int nslot) {
+        constexpr int FR = decltype(frc)::value, EN = decltype(enc)::value;
         const char *ab = lds + slot * L::A_STAGE + op_a;
         const char *bb = lds + (st & 1) * L::B_BUF + op_b;
-        bf16x8 fa[2][2], fb[2][2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int p = 2 * ks + oh;
-#pragma unroll
-            for (int a = 0; a < 2; ++a) fa[ks][a] = *(const bf16x8 *)(ab + a * 32 * 64 + 16 * (p ^ aswz));
-#pragma unroll
-            for (int b = 0; b < 2; ++b) fb[ks][b] = *(const bf16x8 *)(bb + b * 32 * GR_BROW * 2 + 16 * p);
-        }
         const float *sc = (const float *)(lds + slot * L::SZ_STAGE + op_s);
-        float s0[2], s1[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            s0[b] = sc[32 * b];
-            s1[b] = sc[GM_BN + 32 * b];
-        }
+        for (int ks = 0; ks < KS; ++ks) {
+            const int p = 2 * ks + oh;
+            bf16x8 fa[2], fb[2];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < 2; ++a) fa[a] = *(const bf16x8 *)(ab + a * 32 * L::AROW + 16 * (p ^ aswz));
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                dg[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][a], fb[0][b], F0 ? f32x16{} : dg[a][b], 0, 0, 0);
-        if constexpr (MID) {
+            for (int b = 0; b < 2; ++b) fb[b] = *(const bf16x8 *)(bb + b * 32 * L::BROW * 2 + 16 * p);
+            const bool fresh = (FR >> ks) & 1;
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
+                    dg[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], fresh ? f32x16{} : dg[a][b], 0,
+                                                                       0, 0);
+            if ((EN >> ks) & 1) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(s0[b], dg[a][b][r], acc[a][b][r]);
+                for (int b = 0; b < 2; ++b) {
+                    const float s = sc[ks * GM_BN + 32 * b];
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(s, dg[a][b][r], acc[a][b][r]);
+                }
+                // a group starting at the next step overwrites D: keep its
+                // products behind these reads
+                if (ks + 1 < KS && ((FR >> (ks + 1)) & 1)) __builtin_amdgcn_sched_barrier(0);
+            }
         }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                dg[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][a], fb[1][b], MID ? f32x16{} : dg[a][b], 0, 0, 0);
         dequant(nslot, (st + 1) & 1);
-        if constexpr (E1) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(s1[b], dg[a][b][r], acc[a][b][r]);
-        }
     };
 
-    // Ring: stage j lives in slot j % NST.  At the end of every stage
-    // iteration c every stage up to c + 2 has landed (NST - 3 stages of loads
-    // may still be outstanding); stages issued past the end re-read the last
-    // one, unused (the dequantization of the stage after the last one writes
-    // a weight tile that is never read).
-    static_assert(NST >= 4, "the ring needs the stage computed, the next one and one in flight");
+    // Ring: stage j lives in slot j % NST.  Loads go out in stage order, each
+    // stage's packed words and scales before its activations; at the end of
+    // iteration c the next stage's words and scales (stage c + 2 in the ring:
+    // its conversions run in iteration c + 1) and stage c + 1's activations
+    // have landed, so stage c + 2's activations and everything later may
+    // still be outstanding.  Stages issued past the end re-read the last one,
+    // unused (the dequantization of the stage after the last one writes a
+    // weight tile that is never read).
     constexpr int PS = L::PER_STAGE;
     for (int st = 0; st < NST - 1; ++st) issue(st);
-    gr_wait_vm<(NST - 2) * PS>();   // stage 0
+    gr_wait_vm<ADMA + (NST - 2) * PS>();   // stage 0's words and scales
     gr_barrier();
     dequant(0, 0);
-    gr_wait_vm<(NST - 3) * PS>();   // stage 1
+    gr_wait_vm<ADMA + (NST - 3) * PS>();   // stage 0's activations, stage 1's words and scales
     gr_barrier();
     int c = 0, slot = 0;
-    auto iteration = [&](auto f0c, auto midc, auto e1c) {
+    auto iteration = [&](auto frc, auto enc) {
         const int next = slot == NST - 1 ? 0 : slot + 1;
         issue(slot == 0 ? NST - 1 : slot - 1);   // stage c + NST - 1, into the slot of stage c - 1
-        stage(f0c, midc, e1c, c, slot, next);
-        gr_wait_vm<(NST - 3) * PS>();            // stage c + 2
+        stage(frc, enc, c, slot, next);
+        gr_wait_vm<ADMA + (NST - 3) * PS>();
         gr_barrier();
         slot = next;
         ++c;
     };
-    using T = std::true_type;
-    using F = std::false_type;
+    using IC0 = std::integral_constant<int, 0>;
+    using ICA = std::integral_constant<int, (1 << KS) - 1>;            // every step
+    using ICF = std::integral_constant<int, 1>;                        // first step
+    using ICL = std::integral_constant<int, 1 << (KS - 1)>;            // last step
+    using ICE = std::integral_constant<int, KS == 4 ? 0b0101 : 0b01>;  // even steps
+    using ICO = std::integral_constant<int, KS == 4 ? 0b1010 : 0b10>;  // odd steps
     if (gsteps == 1) {
         // groups of 16: each k step is a group
-        while (c < nst) iteration(T{}, T{}, T{});
+        while (c < nst) iteration(ICA{}, ICA{});
+    } else if (gsteps == 2 && KS == 4) {
+        // groups of 32 in stages of 64: two per stage
+        while (c < nst) iteration(ICE{}, ICO{});
     } else {
-        // groups of whole stages (g a multiple of 32, or one group per row)
-        const int spg = gsteps / 2;
+        // groups of whole stages (or one group per row)
+        const int spg = gsteps / KS;
         while (c < nst) {
             const int len = std::min(spg, nst - c);
             if (len == 1) {
-                iteration(T{}, F{}, T{});
+                iteration(ICF{}, ICL{});
             } else {
-                iteration(T{}, F{}, F{});
-                for (int j = 1; j < len - 1; ++j) iteration(F{}, F{}, F{});
-                iteration(F{}, F{}, T{});
+                iteration(ICF{}, IC0{});
+                for (int j = 1; j < len - 1; ++j) iteration(IC0{}, IC0{});
+                iteration(IC0{}, ICL{});
             }
         }
     }
@@ -966,13 +975,23 @@ __global__ __launch_bounds__(64 * NW) void dq_gemm_ring_kernel(const uint16_t *_
         }
 }
 
-// the streamed form needs whole units, groups of 16 or of whole units (or
-// one group per row) and 32-bit buffer offsets (a row tile of activations,
-// the packed words, the scales)
-bool gemm_ring_ok(int64_t d_in, int64_t d_out, int bits, int g) {
+// the streamed form in stages of KC: whole stages, groups of 16, of 32 (or
+// of whole stages, or one group per row), codes of up to 4 bits for stages
+// of 64, and 32-bit buffer offsets (a row tile of activations, the packed
+// words, the scales)
+bool gemm_ring_ok(int kc, int64_t d_in, int64_t d_out, int bits, int g) {
     const int64_t lim = (int64_t)1 << 31;
-    return d_in % GR_KC == 0 && (g == 16 || g % GR_KC == 0 || g == d_in) && (int64_t)GM_BM * d_in * 2 < lim &&
+    if (kc == 64 && bits > 4) return false;
+    return d_in % kc == 0 && (g == 16 || g == 32 || g % kc == 0 || g == d_in) && (int64_t)GM_BM * d_in * 2 < lim &&
            bits * (d_in / 32) * d_out * 4 < lim && (d_in / 16) * d_out * 4 < lim;
+}
+
+template <int BITS, int KC>
+hipError_t launch_gemm_ring(const uint16_t *A, const DequantArgs &a, int64_t nwords, hipStream_t st) {
+    const dim3 grid((unsigned)cdiv(a.m, GM_BM), (unsigned)cdiv(a.d_out, GM_BN));
+    dq_gemm_ring_kernel<BITS, KC><<<grid, 64 * GR_NW, 0, st>>>(A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.m, a.d_in,
+                                                              a.d_out, a.group, a.ngroups, nwords);
+    return hipGetLastError();
 }
 
 template <int BITS>
@@ -987,12 +1006,10 @@ hipError_t launch_gemm_bits(const DequantArgs &a, hipStream_t st) {
     }
     const dim3 grid((unsigned)cdiv(a.m, GM_BM), (unsigned)cdiv(a.d_out, GM_BN));
     const int64_t nwords = cdiv((int64_t)BITS * a.d_in, 32);
-    if (gemm_ring_ok(a.d_in, a.d_out, BITS, a.group)) {
-        const dim3 rgrid((unsigned)cdiv(a.m, GrLayout<BITS, GR_WAVES>::BM), (unsigned)cdiv(a.d_out, GM_BN));
-        dq_gemm_ring_kernel<BITS, GR_WAVES><<<rgrid, 64 * GR_WAVES, 0, st>>>(
-            A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.m, a.d_in, a.d_out, a.group, a.ngroups, nwords);
-        return hipGetLastError();
+    if constexpr (BITS <= 4) {
+        if (gemm_ring_ok(64, a.d_in, a.d_out, BITS, a.group)) return launch_gemm_ring<BITS, 64>(A, a, nwords, st);
     }
+    if (gemm_ring_ok(32, a.d_in, a.d_out, BITS, a.group)) return launch_gemm_ring<BITS, 32>(A, a, nwords, st);
     dq_gemm_kernel<BITS><<<grid, 512, 0, st>>>(A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.m, a.d_in, a.d_out,
                                                a.group, a.ngroups, nwords);
     return hipGetLastError();

@@ -119,6 +119,12 @@ EXACT_CASES = [   # (d_out, d_in, bits, g, m, act_order, a_dtype, seed)
     (130, 160, 2, 16, 17, True, "bf16", 28),     # groups of 16, two per stage
     (257, 64, 8, 16, 20, False, "bf16", 29),     # two stages only: most of the ring issued past the end
     (200, 480, 4, 48, 33, True, "bf16", 30),     # groups of 48 ending mid-stage
+    # stages of 64 (codes up to 4 bits, d_in % 64 == 0)
+    (300, 1024, 3, 32, 300, True, "bf16", 31),   # groups of 32: two per stage, ragged tiles
+    (130, 192, 2, 16, 17, True, "bf16", 32),     # groups of 16: four per stage
+    (257, 128, 4, -1, 20, False, "bf16", 33),    # one group per row over two stages
+    (96, 64, 2, 64, 40, True, "bf16", 34),       # a single stage: the ring longer than the row
+    (200, 576, 4, 96, 33, True, "bf16", 35),     # groups of 96: stages of 32, three per group
 ]
 
 
