@@ -222,8 +222,8 @@ GPTQ_API gptq_status gptq_inverse_factor(const float *H, int64_t d_in, float dam
  * workspace  device scratch of gptq_dequant_matmul_workspace_size(m, d_out,
  *            d_in, bits, group_size) bytes (0 when m == 0; may then be NULL).
  *            It holds the k-ranges' partial sums and one completion counter
- *            per 256 output rows: it must be ZEROED before its first use;
- *            every call leaves it ready for the next (counters back at zero).
+ *            per output tile: it must be ZEROED before its first use; every
+ *            call leaves it ready for the next (counters back at zero).
  *            A workspace serves one call at a time.
  * m == 0 is a no-op.  Errors: EINVAL (bad sizes, bits, group_size or dtype,
  * NULL pointer; nothing launched), ENOMEM (workspace too small), EHIP.

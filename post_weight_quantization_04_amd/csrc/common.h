@@ -141,7 +141,7 @@ struct DequantArgs {
     void *Y;                // [m][d_out]
     int y_bf16;             // Y is bf16 (else fp32)
     float *part;            // workspace: partial sums of the k-ranges
-    int32_t *counters;      // workspace: one per 256-row tile, zero between calls
+    int32_t *counters;      // workspace: one per output tile, zero between calls
     uint16_t *ap;           // workspace: activations in processing order (wide path)
     int64_t m, d_in, d_out;
     int bits, group;        // group: effective group size

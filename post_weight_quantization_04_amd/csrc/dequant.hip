@@ -643,7 +643,8 @@ __global__ __launch_bounds__(512) void dq_gemm_kernel(const uint16_t *__restrict
 // on distinct banks.  Waves with no packed-word load of their own in a stage
 // issue a dummy one, so that every wave counts the same loads per stage.
 // ---------------------------------------------------------------------------
-constexpr int GR_NW = 8;   // waves per work group
+constexpr int GR_NW = 8;          // waves per work group
+constexpr int GR_MAX_SPLIT = 16;  // k splits of a small grid, at most
 
 template <int BITS, int KC>
 struct GrLayout {
@@ -701,14 +702,20 @@ __device__ __forceinline__ int gr_swz(int row) {
         return ((row >> 1) ^ ((row & 1) << 2)) & 7;
 }
 
-template <int BITS, int KC>
+// Split k (small grids): work group z takes stages [st_begin, st_end), cut
+// at multiples of `align` stages (whole groups), folds its own pieces of the
+// groups (s D is linear in D), and the tile's last group to finish adds the
+// splits' partial sums in split order.
+template <int BITS, int KC, bool SPLIT>
 __global__ __launch_bounds__(64 * GR_NW) void dq_gemm_ring_kernel(const uint16_t *__restrict__ A,
                                                                   const uint32_t *__restrict__ Q,
                                                                   const float *__restrict__ scales,
                                                                   const float *__restrict__ zeros,
                                                                   void *__restrict__ Y, int y_bf16, int64_t m,
                                                                   int64_t d_in, int64_t d_out, int g, int ngroups,
-                                                                  int64_t nwords) {
+                                                                  int64_t nwords, float *__restrict__ part,
+                                                                  int32_t *__restrict__ counters, int nsplit,
+                                                                  int align) {
     using L = GrLayout<BITS, KC>;
     // (arrays that the lambdas below capture have literal sizes, their
     // largest counts: with value-dependent sizes the host pass drops the
@@ -717,11 +724,22 @@ __global__ __launch_bounds__(64 * GR_NW) void dq_gemm_ring_kernel(const uint16_t
     static_assert(ADMA <= 4 && QDMA <= 2 && SDMA <= 2 && NCH <= 2, "per-thread array bounds");
     constexpr int RPI = 1024 / L::AROW, PPR = L::AROW / 16;   // activation rows per load, pieces per row
     __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+    __shared__ int last_flag;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.x * GM_BM, n0 = (int64_t)blockIdx.y * GM_BN;
-    const int nst = (int)(d_in / KC);
+    const int split = SPLIT ? (int)blockIdx.z : 0;
+    const int nst_all = (int)(d_in / KC);
+    int st_begin = 0, st_end = nst_all;
+    if (SPLIT) {
+        // (32-bit arithmetic, kept in scalar registers: the loads' scalar
+        // offsets derive from these)
+        const int nal = nst_all / align;
+        st_begin = __builtin_amdgcn_readfirstlane(align * (nal * split / nsplit));
+        st_end = __builtin_amdgcn_readfirstlane(split == nsplit - 1 ? nst_all : align * (nal * (split + 1) / nsplit));
+    }
+    const int nst = st_end - st_begin;   // this split's stages
 
     // Every load address is clamped into its operand (rows past m re-read
     // the last row, columns past d_out the last column, stages past the end
@@ -764,10 +782,11 @@ __global__ __launch_bounds__(64 * GR_NW) void dq_gemm_ring_kernel(const uint16_t
     const int qstride = L::UPS * BITS * (int)d_out * 4, gstride = (int)d_out * 4;
     // issue tracker: the stage to issue (clamped when loaded), the group of
     // its first k step and that step's place in the group
-    int iss_st = 0, iss_g = 0, iss_r = 0;
+    int iss_st = st_begin, iss_g = __builtin_amdgcn_readfirstlane(st_begin * KS / gsteps);
+    int iss_r = __builtin_amdgcn_readfirstlane(st_begin * KS - iss_g * gsteps);
 
     auto issue = [&](int slot) {
-        const int st = std::min(iss_st, nst - 1);
+        const int st = std::min(iss_st, st_end - 1);
         // packed words and scales first: the next stage's conversions need
         // them one stage before its products need the activations
         char *qbase = lds + L::Q_OFF + slot * L::Q_STAGE;
@@ -954,6 +973,95 @@ __global__ __launch_bounds__(64 * GR_NW) void dq_gemm_ring_kernel(const uint16_t
     gr_wait_vm<0>();   // no load may still write LDS when the group ends
 
     // Y: tile (a, b) of wave (wm, wn), register 4 i + j <-> row 8 i + 4 (l / 32) + j, column l % 32
+    auto store_y = [&](int64_t row, int64_t n, float v) {
+        if (y_bf16) {
+            const unsigned u = __builtin_bit_cast(unsigned, v);
+            ((uint16_t *)Y)[row * d_out + n] = (uint16_t)((u + ((u >> 16) & 1u) + 0x7FFFu) >> 16);
+        } else {
+            ((float *)Y)[row * d_out + n] = v;
+        }
+    };
+    if constexpr (SPLIT) {
+        // This split's partial sums, then the tile's last group adds them
+        // all.  Device-scope atomic stores and loads (written through to, and
+        // read from, the point where all XCDs see memory alike), every store
+        // drained (vmcnt) before the group's count is added: the ordering of
+        // a device-scope release and acquire without writing back and
+        // invalidating the whole L2 in every group.
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int64_t n = n0 + wn * 64 + 32 * b + orow;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = m0 + wm * 64 + 32 * a + 8 * (r >> 2) + 4 * oh + (r & 3);
+                    if (n < d_out && row < m)
+                        __hip_atomic_store(&part[((int64_t)split * m + row) * d_out + n], acc[a][b][r],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int tile = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = old == nsplit - 1;
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        // every split's partial sums (this group's own included: the
+        // accumulators are reused for the sum), one split at a time with
+        // all of the lane's 64 outputs in flight together, added in split
+        // order
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+        // (32-bit element offsets: m d_out is small whenever k is split)
+        int eo[2][16];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = (int)std::min<int64_t>(n0 + wn * 64 + 32 * b + orow, d_out - 1);
+                const int row = (int)std::min<int64_t>(m0 + wm * 64 + 8 * (r >> 2) + 4 * oh + (r & 3), m - 1);
+                eo[b][r] = row * (int)d_out + n;
+            }
+        const int md = (int)(m * d_out);
+#pragma unroll 1
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float *ps = part + (int64_t)sp * md;
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                // rows of block a past m re-read row m - 1 (never stored)
+                f32x16 t[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = a == 0 ? eo[b][r] : std::min(eo[b][r] + 32 * (int)d_out, md - 1);
+                        t[b][r] = __hip_atomic_load(ps + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] += t[b];
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int64_t n = n0 + wn * 64 + 32 * b + orow;
+                if (n >= d_out) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = m0 + wm * 64 + 32 * a + 8 * (r >> 2) + 4 * oh + (r & 3);
+                    if (row < m) store_y(row, n, acc[a][b][r]);
+                }
+            }
+        if (tid == 0) counters[tile] = 0;   // ready for the next call on this workspace
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -964,13 +1072,7 @@ __global__ __launch_bounds__(64 * GR_NW) void dq_gemm_ring_kernel(const uint16_t
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * 64 + 32 * a + 8 * (r >> 2) + 4 * oh + (r & 3);
                 if (row >= m) continue;
-                const float v = acc[a][b][r];
-                if (y_bf16) {
-                    const unsigned u = __builtin_bit_cast(unsigned, v);
-                    ((uint16_t *)Y)[row * d_out + n] = (uint16_t)((u + ((u >> 16) & 1u) + 0x7FFFu) >> 16);
-                } else {
-                    ((float *)Y)[row * d_out + n] = v;
-                }
+                store_y(row, n, acc[a][b][r]);
             }
         }
 }
@@ -986,11 +1088,35 @@ bool gemm_ring_ok(int kc, int64_t d_in, int64_t d_out, int bits, int g) {
            bits * (d_in / 32) * d_out * 4 < lim && (d_in / 16) * d_out * 4 < lim;
 }
 
+// k splits of the wide path for a small grid (fewer tiles than half the
+// CUs), each split at least four stages of 32: at most
+// this many (the workspace holds their partial sums); a launch may take
+// fewer so that splits hold whole groups
+int gemm_splits(int64_t m, int64_t d_out, int64_t d_in) {
+    const int64_t tiles = cdiv(m, GM_BM) * cdiv(d_out, GM_BN);
+    if (tiles >= 128) return 1;
+    int64_t s = cdiv(256, tiles);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, d_in / 32 / 4));
+    return (int)std::min<int64_t>(s, GR_MAX_SPLIT);
+}
+
 template <int BITS, int KC>
 hipError_t launch_gemm_ring(const uint16_t *A, const DequantArgs &a, int64_t nwords, hipStream_t st) {
-    const dim3 grid((unsigned)cdiv(a.m, GM_BM), (unsigned)cdiv(a.d_out, GM_BN));
-    dq_gemm_ring_kernel<BITS, KC><<<grid, 64 * GR_NW, 0, st>>>(A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16, a.m, a.d_in,
-                                                              a.d_out, a.group, a.ngroups, nwords);
+    // splits hold whole groups: stages per group when a group spans several
+    // stages (one group per row may split anywhere: its fold is linear)
+    const int gsteps = a.group / 16, ks = KC / 16;
+    const int align = (gsteps > ks && a.group != a.d_in) ? gsteps / ks : 1;
+    const int nal = (int)(a.d_in / KC) / align;
+    const int nsplit = std::max(1, std::min(gemm_splits(a.m, a.d_out, a.d_in), nal));
+    const dim3 grid((unsigned)cdiv(a.m, GM_BM), (unsigned)cdiv(a.d_out, GM_BN), (unsigned)nsplit);
+    if (nsplit > 1)
+        dq_gemm_ring_kernel<BITS, KC, true><<<grid, 64 * GR_NW, 0, st>>>(A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16,
+                                                                        a.m, a.d_in, a.d_out, a.group, a.ngroups,
+                                                                        nwords, a.part, a.counters, nsplit, align);
+    else
+        dq_gemm_ring_kernel<BITS, KC, false><<<grid, 64 * GR_NW, 0, st>>>(A, a.Q, a.scales, a.zeros, a.Y, a.y_bf16,
+                                                                         a.m, a.d_in, a.d_out, a.group, a.ngroups,
+                                                                         nwords, a.part, a.counters, 1, 1);
     return hipGetLastError();
 }
 
@@ -1031,8 +1157,15 @@ DequantWs dequant_ws_layout(int64_t m, int64_t d_out, int64_t d_in, int bits) {
         const int s = gemv_splits(M, d_out, d_in, bits);
         if (s > 1) part = std::max(part, (size_t)s * M * d_out * sizeof(float));
     }
+    size_t ncount = (size_t)cdiv(d_out, GV_ROWS);
+    if (m >= GM_MIN_M) {
+        // the wide path's split partial sums and one counter per tile
+        const int s = gemm_splits(m, d_out, d_in);
+        if (s > 1) part = std::max(part, (size_t)s * m * d_out * sizeof(float));
+        ncount = std::max(ncount, (size_t)(cdiv(m, GM_BM) * cdiv(d_out, GM_BN)));
+    }
     w.counters_off = align256(part);
-    w.counters_bytes = (size_t)cdiv(d_out, GV_ROWS) * sizeof(int32_t);
+    w.counters_bytes = ncount * sizeof(int32_t);
     w.ap_off = align256(w.counters_off + w.counters_bytes);
     const size_t ap = m >= GM_MIN_M ? (size_t)m * d_in * sizeof(uint16_t) : 0;
     w.bytes = m > 0 ? align256(w.ap_off + ap) : 0;
