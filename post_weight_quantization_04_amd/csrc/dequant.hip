@@ -484,6 +484,45 @@ __global__ __launch_bounds__(256) void dq_permute_kernel(const uint16_t *__restr
     Ap[idx] = A[i * d_in + perm[k]];
 }
 
+// The same, one work group per activation row (d_in % 8 == 0): the row is
+// staged in LDS with 16-byte loads, gathered from there and written as
+// 16-byte pieces (a gather straight from global memory touches a scattered
+// 2-byte value per lane).
+constexpr int64_t PERMUTE_LDS_MAX = 80 * 1024;   // bf16 values of a staged row (160 KB)
+__global__ __launch_bounds__(256) void dq_permute_lds_kernel(const uint16_t *__restrict__ A,
+                                                             const int32_t *__restrict__ perm,
+                                                             uint16_t *__restrict__ Ap, int64_t d_in) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t srow16[];
+    const int64_t i = blockIdx.x;
+    const int np = (int)(d_in / 8);
+    const u32x4 *src = (const u32x4 *)(A + i * d_in);
+    for (int p = threadIdx.x; p < np; p += 256) *(u32x4 *)(srow16 + 8 * p) = src[p];
+    __syncthreads();
+    u32x4 *dst = (u32x4 *)(Ap + i * d_in);
+    for (int p = threadIdx.x; p < np; p += 256) {
+        int c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = perm[8 * p + e];
+        unsigned w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (unsigned)srow16[c[2 * e]] | ((unsigned)srow16[c[2 * e + 1]] << 16);
+        dst[p] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// dynamic LDS above the default limit must be allowed once
+bool permute_lds_ok(int64_t d_in) {
+    static int state = 0;   // 0 unknown, 1 allowed, -1 refused
+    if (d_in > PERMUTE_LDS_MAX) return false;
+    if (state == 0)
+        state = hipFuncSetAttribute((const void *)dq_permute_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(PERMUTE_LDS_MAX * 2)) == hipSuccess
+                    ? 1
+                    : -1;
+    if (state < 0) (void)hipGetLastError();
+    return state > 0;
+}
+
 // d_in % 8 == 0 (whole 16-byte pieces of activation rows)
 template <int BITS>
 __global__ __launch_bounds__(512) void dq_gemm_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Q,
@@ -1124,8 +1163,12 @@ template <int BITS>
 hipError_t launch_gemm_bits(const DequantArgs &a, hipStream_t st) {
     const uint16_t *A = (const uint16_t *)a.A;
     if (a.perm) {
-        const int64_t n = a.m * a.d_in;
-        dq_permute_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(A, a.perm, a.ap, a.m, a.d_in);
+        if (permute_lds_ok(a.d_in)) {
+            dq_permute_lds_kernel<<<(unsigned)a.m, 256, (size_t)a.d_in * 2, st>>>(A, a.perm, a.ap, a.d_in);
+        } else {
+            const int64_t n = a.m * a.d_in;
+            dq_permute_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(A, a.perm, a.ap, a.m, a.d_in);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         A = a.ap;
