@@ -161,17 +161,19 @@ __device__ __forceinline__ void wait_vm_left(int left) {
     }
 }
 
-// Instruction order for the second half of a stage: the next stage's first
-// operand reads go out between the first MFMAs, then one refill DMA per one
-// or two MFMAs, so that a DMA waiting for queue space never holds back a long
-// run of MFMAs.  (The reads must precede the DMAs: LDS aliasing is unknown to
-// the compiler.)
+// Instruction order for each half of a stage (16 MFMAs): the next half's 16
+// operand reads go out two per MFMA over the first eight, then the half's
+// share of the refill DMAs, one per one or two MFMAs.  Reads in a burst (four
+// per MFMA) or DMAs mixed in among them queue up behind each other in LDS and
+// leave the matrix core waiting; spread this way the product runs ≈ 8%
+// faster.  (The reads must precede the DMAs: LDS aliasing is unknown to the
+// compiler.)
 template <int NDMA>
 __device__ __forceinline__ void interleave_refill() {
     constexpr int MFMA = 0x008, VMEM = 0x010, DSR = 0x100;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(DSR, 4, 0);
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
     }
 #pragma unroll
@@ -179,7 +181,6 @@ __device__ __forceinline__ void interleave_refill() {
         __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
         __builtin_amdgcn_sched_group_barrier(MFMA, 8 / NDMA, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
 }
 
 // One (split, tile) unit over tokens [k0, k1).  DIAG: I == J, only the A slab
@@ -227,11 +228,11 @@ __device__ __forceinline__ void bf16_unit(const uint16_t *__restrict__ X, int64_
             dma_off[q] = (int)((row * d + unit * 8) * 2);
         }
     }
-    auto dma = [&](int st) {
+    auto dma_part = [&](int st, int q0, int q1) {
         const int stage_off = (int)((int64_t)st * BBK * d * 2);
         lds_void_t *buf = (lds_void_t *)(smem + (st % NBUF) * 2 * SLAB);
 #pragma unroll
-        for (int q = 0; q < BBK / 8; ++q) {
+        for (int q = q0; q < q1; ++q) {
             const int chunk = wave * (BBK / 8) + q;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)((lds_char *)buf + chunk * 1024), 16,
                                                      dma_off[q] + stage_off + I * BT * 2, 0, 0, 0);
@@ -240,6 +241,7 @@ __device__ __forceinline__ void bf16_unit(const uint16_t *__restrict__ X, int64_
                                                          16, dma_off[q] + stage_off + J * BT * 2, 0, 0, 0);
         }
     };
+    auto dma = [&](int st) { dma_part(st, 0, BBK / 8); };
     auto reg_issue = [&](int st) {
         if (st >= nst) return;
         const int64_t k = k0 + (int64_t)st * BBK;
@@ -302,26 +304,41 @@ __device__ __forceinline__ void bf16_unit(const uint16_t *__restrict__ X, int64_
     // one waited for are always in flight (past the end they load zeros).
     // Each barrier is passed only once every wave has finished reading the
     // stage before it (lds_barrier drains this wave's LDS reads), so that
-    // stage's buffer is refilled right after the barrier.
+    // stage's buffer is free from there on: half of its refill goes out with
+    // the MFMAs after the barrier, the other half with the next half stage's
+    // (DMA writes spread over the whole stage instead of crowding LDS in one
+    // half).  Every stage is wholly issued before the wait that counts it.
     static_assert(BBK == 32, "two k steps per stage");
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
     if (nst > 0) {
         wait_vm_left((NBUF - 2) * per_stage);                   // stage 0 landed
         lds_barrier();
-        issue(NBUF - 1);                                         // the one buffer still free
+        if (VEC)
+            dma_part(NBUF - 1, 0, BBK / 16);                     // the one buffer still free: first half
+        else
+            issue(NBUF - 1);
         frags(0, 0, fa0, fb0);
         for (int st = 0; st < nst - 1; ++st) {
             frags(st, 1, fa1, fb1);
-            mfma16(fa0, fb0);
+            if (VEC) {
+                dma_part(st - 1 + NBUF, BBK / 16, BBK / 8);      // second half of the refill begun before
+                mfma16(fa0, fb0);
+                interleave_refill<per_stage / 2>();
+            } else {
+                mfma16(fa0, fb0);
+            }
             // keep the first half's MFMAs ahead of the wait and the barrier
             __builtin_amdgcn_sched_barrier(0);
             wait_vm_left((NBUF - 2) * per_stage);               // stage st+1 landed
             lds_barrier();                                       // all reads of stage st are done
             __builtin_amdgcn_sched_barrier(0);
             frags(st + 1, 0, fa0, fb0);
-            issue(st + NBUF);                                    // into the buffer of stage st
+            if (VEC)
+                dma_part(st + NBUF, 0, BBK / 16);                // first half of the refill of stage st's buffer
+            else
+                issue(st + NBUF);                                // into the buffer of stage st
             mfma16(fa1, fb1);
-            if (VEC) interleave_refill<per_stage>();
+            if (VEC) interleave_refill<per_stage / 2>();
             __builtin_amdgcn_sched_barrier(0);
         }
         frags(nst - 1, 1, fa1, fb1);
