@@ -309,6 +309,24 @@ __device__ __forceinline__ void bf16_unit(const uint16_t *__restrict__ X, int64_
     // (DMA writes spread over the whole stage instead of crowding LDS in one
     // half).  Every stage is wholly issued before the wait that counts it.
     static_assert(BBK == 32, "two k steps per stage");
+    if (DIAG && VEC && wr < wc) {
+        // The wave above the diagonal of a diagonal tile: its quadrant is never
+        // stored, so it only moves its share of every stage and meets every
+        // barrier of the others (same DMA order, same waits).
+        if (nst > 0) {
+            wait_vm_left((NBUF - 2) * per_stage);
+            lds_barrier();
+            dma_part(NBUF - 1, 0, BBK / 16);
+            for (int st = 0; st < nst - 1; ++st) {
+                dma_part(st - 1 + NBUF, BBK / 16, BBK / 8);
+                wait_vm_left((NBUF - 2) * per_stage);
+                lds_barrier();
+                dma_part(st + NBUF, 0, BBK / 16);
+            }
+            wait_vm<0>();
+        }
+        return;
+    }
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
     if (nst > 0) {
         wait_vm_left((NBUF - 2) * per_stage);                   // stage 0 landed
@@ -346,7 +364,8 @@ __device__ __forceinline__ void bf16_unit(const uint16_t *__restrict__ X, int64_
         mfma16(fa1, fb1);
         wait_vm<0>();   // stages issued past the end must land before the group's LDS is released
     }
-    // the wave above the diagonal of a diagonal tile computed nothing useful
+    // (register-staged path) the wave above the diagonal of a diagonal tile
+    // computed nothing useful
     if (DIAG && wr < wc) return;
     // accumulator layout: lane (h, li), register 4a+b <-> row 8a+4h+b, column li
 #pragma unroll
