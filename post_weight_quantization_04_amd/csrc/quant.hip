@@ -96,7 +96,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *p, int6
 // instruction) hit 64 distinct banks.  Wave w takes column tiles 16w and
 // 16w + 64 on v_mfma_f32_16x16x4_f32 (A[i][k] at lane i + 16k, B[k][j] at
 // lane j + 16k, D[i][j] at lane 16 (i/4) + j, register i % 4), its
-// accumulators kept across all chunks.
+// accumulators kept across all chunks.  They hold -W and add E U (negation
+// is exact, so the result is bitwise that of W - E U): the operands then go
+// from LDS to the MFMAs untouched, and every read of a chunk is issued before
+// its first product instead of each pair waiting for its own reads.
 __device__ __forceinline__ void near_update_ring(float *Wl, int LW, float *ring, const float *u, const float *En,
                                                  int64_t row0, int64_t d_in, int64_t d_out, int nk) {
     const int tid = threadIdx.x;
@@ -134,8 +137,8 @@ __device__ __forceinline__ void near_update_ring(float *Wl, int LW, float *ring,
     f32x4 acc0, acc1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        acc0[r] = Wl[(4 * lk + r) * LW + jp + li];
-        acc1[r] = Wl[(4 * lk + r) * LW + j1 + li];
+        acc0[r] = -Wl[(4 * lk + r) * LW + jp + li];
+        acc1[r] = -Wl[(4 * lk + r) * LW + j1 + li];
     }
     // this lane's U columns jp + li and j1 + li, swizzled by its k-row's r % 4 = lk
     const int cu0 = 4 * (((jp + li) >> 2) ^ (4 * lk)) + (li & 3);
@@ -152,7 +155,7 @@ __device__ __forceinline__ void near_update_ring(float *Wl, int LW, float *ring,
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int k = 4 * t + lk;
-            ea[t] = -st[NUF + k * QROWS + li];
+            ea[t] = st[NUF + k * QROWS + li];
             ub0[t] = st[k * 128 + cu0];
             ub1[t] = st[k * 128 + cu1];
         }
@@ -161,11 +164,13 @@ __device__ __forceinline__ void near_update_ring(float *Wl, int LW, float *ring,
             acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub0[t], acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[t], ub1[t], acc1, 0, 0, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 48, 0);   // every operand read of the chunk
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);   // then its MFMAs
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        Wl[(4 * lk + r) * LW + jp + li] = acc0[r];
-        Wl[(4 * lk + r) * LW + j1 + li] = acc1[r];
+        Wl[(4 * lk + r) * LW + jp + li] = -acc0[r];
+        Wl[(4 * lk + r) * LW + j1 + li] = -acc1[r];
     }
 }
 
@@ -264,8 +269,16 @@ __device__ __forceinline__ void load_coef(const float *Ul, const float *uil, int
         ui[4 * q + 2] = x.z;
         ui[4 * q + 3] = x.w;
     }
+    // row c0 + S of the packed block starts at column c0 + 4 floor(S/4) and
+    // holds Bp - c0 - 4 floor(S/4) values: walk the row starts by adding
+    // lengths (uniform) instead of evaluating the packed offset per row
+    int start = uoff(c0, Bp);
 #pragma unroll
-    for (int S = 0; S < CH; ++S) u[S] = Ul[uidx(c0 + S, c0, Bp) + max(cl, S)];
+    for (int S = 0; S < CH; ++S) {
+        const int q4 = 4 * (S >> 2);
+        u[S] = Ul[start + max(cl, S) - q4];
+        start += Bp - c0 - q4;
+    }
 }
 
 // Block [b, e) for this group's 16 rows.  a.E is the block's error slot and
@@ -516,11 +529,25 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
                         mx = fmaxf(mx, v);
                     }
             } else {
+                // the group's columns from the staged tile, all reads in
+                // flight together: lanes past the group's end reread its last
+                // column, which leaves min and max unchanged
                 const int gl = std::min(g, nb - c0);
-                for (int j = c; j < gl; j += CH) {
-                    const float v = Wl[rl * LW + c0 + j];
-                    mn = fminf(mn, v);
-                    mx = fmaxf(mx, v);
+                const float *wr = Wl + rl * LW + c0;
+                if (gl <= 8 * CH) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float v = wr[min(c + CH * q, gl - 1)];
+                        mn = fminf(mn, v);
+                        mx = fmaxf(mx, v);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const float v = wr[min(c + CH * q, gl - 1)];
+                        mn = fminf(mn, v);
+                        mx = fmaxf(mx, v);
+                    }
                 }
             }
             minmax16(mn, mx);
