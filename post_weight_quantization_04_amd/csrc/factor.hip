@@ -64,6 +64,7 @@ constexpr int NB = FACT_NB;   // 128
 //               S_ib = P_i X_bb,
 // with S_ij = sum_{m=j}^{i-1} L_im M_mj held in the consumed lower blocks.
 // Block products are 32x32x32 on v_mfma_f32_32x32x2_f32, one per wave.
+// Wave 0 runs potrf32 of sub-block b+1 during step b's trailing products.
 // Rows/cols at or past kb hold the identity.
 // ---------------------------------------------------------------------------
 constexpr int FLD = NB + 1;   // LDS row stride of the 128x128 block (floats)
@@ -266,10 +267,14 @@ __device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base,
                                                 float *bc) {
     const int wave = threadIdx.x >> 6;
     constexpr int SB = 32, NSB = NB / SB;
+    // Sub-block b + 1's own chain needs only its diagonal block's update from
+    // step b, so wave 0 takes that one trailing product and goes straight on
+    // to potrf32 of b + 1 while waves 1-3 take the rest of step b's trailing
+    // products (the chain of one wave is most of the routine's time).
+    if (wave == 0) potrf32(F, 0, kb, info_base, info, bc);
+    __syncthreads();
     for (int b = 0; b < NSB; ++b) {
         const int s = SB * b;
-        if (wave == 0) potrf32(F, s, kb, info_base, info, bc);
-        __syncthreads();
         // panel blocks i = b+1.. (transposed into block (b, i)) and inverse rows j < b
         {
             const int ntask = (NSB - 1 - b) + b;
@@ -289,37 +294,46 @@ __device__ __forceinline__ void potrf_block_lds(float *F, int kb, int info_base,
             }
         }
         __syncthreads();
-        // trailing Cholesky blocks (i, c), b < c <= i, then inverse sums (i, j), j <= b
-        {
-            const int nr = NSB - 1 - b;
-            const int nchol = nr * (nr + 1) / 2;
-            const int ntask = nchol + nr * (b + 1);
-            for (int t = wave; t < ntask; t += 4) {
-                f32x16 acc;
-                if (t < nchol) {
-                    int ii = 0;
-                    while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
-                    const int i = b + 1 + ii, cc = b + 1 + (t - ii * (ii + 1) / 2);
-                    blk_load(acc, F, SB * i, SB * cc);
-                    // A_ic -= P_i P_c^T with P_x(m, k) at F[(s + k) * FLD + 32x + m]
-                    f32x16 prod = f32x16{};
-                    blk_mfma(prod, F, s * FLD + SB * i, 1, FLD, s * FLD + SB * cc, FLD, 1);
-                    acc -= prod;
-                    blk_store(acc, F, SB * i, SB * cc, 1.f, false);
+        // trailing Cholesky blocks (i, c), b < c <= i, then inverse sums (i, j),
+        // j <= b; task 0 is the next diagonal block (b+1, b+1)
+        const int nr = NSB - 1 - b;
+        const int nchol = nr * (nr + 1) / 2;
+        const int ntask = nchol + nr * (b + 1);
+        auto task = [&](int t) {
+            f32x16 acc;
+            if (t < nchol) {
+                int ii = 0;
+                while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+                const int i = b + 1 + ii, cc = b + 1 + (t - ii * (ii + 1) / 2);
+                blk_load(acc, F, SB * i, SB * cc);
+                // A_ic -= P_i P_c^T with P_x(m, k) at F[(s + k) * FLD + 32x + m]
+                f32x16 prod = f32x16{};
+                blk_mfma(prod, F, s * FLD + SB * i, 1, FLD, s * FLD + SB * cc, FLD, 1);
+                acc -= prod;
+                blk_store(acc, F, SB * i, SB * cc, 1.f, false);
+            } else {
+                const int u = t - nchol;
+                const int i = b + 1 + u / (b + 1), j = u % (b + 1);
+                if (j < b) {
+                    blk_load(acc, F, SB * i, SB * j);
+                    // S_ij += P_i M_bj
+                    blk_mfma(acc, F, s * FLD + SB * i, 1, FLD, s * FLD + SB * j, FLD, 1);
                 } else {
-                    const int u = t - nchol;
-                    const int i = b + 1 + u / (b + 1), j = u % (b + 1);
-                    if (j < b) {
-                        blk_load(acc, F, SB * i, SB * j);
-                        // S_ij += P_i M_bj
-                        blk_mfma(acc, F, s * FLD + SB * i, 1, FLD, s * FLD + SB * j, FLD, 1);
-                    } else {
-                        acc = f32x16{};
-                        // S_ib = P_i X_bb
-                        blk_mfma(acc, F, s * FLD + SB * i, 1, FLD, s * FLD + s, FLD, 1);
-                    }
-                    blk_store(acc, F, SB * i, SB * j, 1.f, false);
+                    acc = f32x16{};
+                    // S_ib = P_i X_bb
+                    blk_mfma(acc, F, s * FLD + SB * i, 1, FLD, s * FLD + s, FLD, 1);
                 }
+                blk_store(acc, F, SB * i, SB * j, 1.f, false);
+            }
+        };
+        if (nr > 0) {
+            if (wave == 0) {
+                // the block is this wave's own: potrf32 reads it after this
+                // wave's stores (a wave's LDS operations complete in order)
+                task(0);
+                potrf32(F, s + SB, kb, info_base, info, bc);
+            } else {
+                for (int t = wave; t < ntask; t += 3) task(t);
             }
         }
         __syncthreads();
