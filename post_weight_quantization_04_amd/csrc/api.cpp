@@ -31,6 +31,18 @@ gptq_status fail(gptq_status s, const char *fmt, ...) {
     return s;
 }
 
+// An enum argument from a C caller (or a foreign-function binding) may hold
+// any int.  Its bits are read as an int, since loading an out-of-range value
+// as the C++ enum type is undefined.
+template <class E>
+int raw(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums here are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool valid_dtype(const gptq_dtype &t) { return raw(t) == GPTQ_F32 || raw(t) == GPTQ_BF16; }
+
 #define HIPCHECK(expr)                                                                      \
     do {                                                                                    \
         hipError_t e_ = (expr);                                                             \
@@ -295,10 +307,15 @@ const char *gptq_profile_stage_name(int stage) {
 
 gptq_status gptq_profile_read(gptq_profile *out, int reset) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    for (auto &p : g_prof.pending) {
+    size_t done = 0;
+    for (; done < g_prof.pending.size(); ++done) {
+        const auto &p = g_prof.pending[done];
         float ms = 0.f;
-        if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
+        if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) {
+            // the pairs already summed go back to the pool exactly once
+            g_prof.pending.erase(g_prof.pending.begin(), g_prof.pending.begin() + done);
             return fail(GPTQ_EHIP, "profile event query failed");
+        }
         g_prof.ms[p.stage] += ms;
         g_prof.launches[p.stage] += 1;
         g_prof.pool.push_back(p.a);
@@ -323,7 +340,7 @@ gptq_status gptq_profile_read(gptq_profile *out, int reset) {
 const char *gptq_last_error(void) { return g_err.c_str(); }
 
 const char *gptq_status_string(gptq_status s) {
-    switch (s) {
+    switch (raw(s)) {
         case GPTQ_OK: return "ok";
         case GPTQ_EINVAL: return "invalid argument";
         case GPTQ_ENOTSPD: return "damped Hessian not positive definite";
@@ -335,7 +352,8 @@ const char *gptq_status_string(gptq_status s) {
 
 int64_t gptq_packed_words(int64_t d_in, int bits) {
     if (d_in < 0 || !valid_bits(bits)) return -1;
-    return cdiv(bits * d_in, 32);
+    // ceil(bits * d_in / 32) without forming bits * d_in (no overflow for any d_in)
+    return (d_in / 32) * bits + cdiv((d_in % 32) * bits, 32);
 }
 
 int64_t gptq_num_groups(int64_t d_in, int group_size) {
@@ -346,7 +364,7 @@ int64_t gptq_num_groups(int64_t d_in, int group_size) {
 }
 
 size_t gptq_hessian_workspace_size(int64_t n, int64_t d_in, gptq_dtype x_dtype) {
-    if (n < 0 || d_in < 1 || d_in > (int64_t)1 << 20 || (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16)) return 0;
+    if (n < 0 || d_in < 1 || d_in > (int64_t)1 << 20 || !valid_dtype(x_dtype)) return 0;
     if (n == 0) return 0;
     return gptq::hessian_ws_bytes(gptq::hessian_plan(n, d_in, x_dtype == GPTQ_BF16));
 }
@@ -354,7 +372,7 @@ size_t gptq_hessian_workspace_size(int64_t n, int64_t d_in, gptq_dtype x_dtype) 
 gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, int64_t n, int64_t d_in, float *H,
                                     void *workspace, size_t workspace_bytes, void *stream) {
     g_err.clear();
-    if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "x_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (!valid_dtype(x_dtype)) return fail(GPTQ_EINVAL, "x_dtype must be GPTQ_F32 or GPTQ_BF16");
     if (n < 0) return fail(GPTQ_EINVAL, "n must be >= 0");
     if (d_in < 1 || d_in > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d_in must be in [1, 2^20]");
     if (!H) return fail(GPTQ_EINVAL, "H is NULL");
@@ -377,7 +395,7 @@ gptq_status gptq_hessian_accumulate(const void *X, gptq_dtype x_dtype, int64_t n
 }
 
 int64_t gptq_hessian_noalloc_max_d_in(gptq_dtype x_dtype) {
-    if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16) return -1;
+    if (!valid_dtype(x_dtype)) return -1;
     // the largest d_in whose lower tiles fit the scratch with one token split
     const gptq::HessPlan p1 = gptq::hessian_plan(1, 1, x_dtype == GPTQ_BF16);
     const int64_t max_slots = (int64_t)(gptq::HESS_STATIC_SCRATCH_BYTES / ((size_t)p1.tile * p1.tile * sizeof(float)));
@@ -389,7 +407,7 @@ int64_t gptq_hessian_noalloc_max_d_in(gptq_dtype x_dtype) {
 gptq_status gptq_hessian_accumulate_noalloc(const void *X, gptq_dtype x_dtype, int64_t n, int64_t d_in, float *H,
                                             void *stream) {
     g_err.clear();
-    if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "x_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (!valid_dtype(x_dtype)) return fail(GPTQ_EINVAL, "x_dtype must be GPTQ_F32 or GPTQ_BF16");
     if (n < 0) return fail(GPTQ_EINVAL, "n must be >= 0");
     if (d_in < 1 || d_in > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d_in must be in [1, 2^20]");
     if (!H) return fail(GPTQ_EINVAL, "H is NULL");
@@ -429,6 +447,8 @@ gptq_status gptq_quantize_layer(const void *W, gptq_dtype w_dtype, int64_t d_out
                                 int bits, int group_size, int block_size, float damp, int act_order,
                                 uint32_t *Qpacked, float *scales, float *zeros, int32_t *perm, void *workspace,
                                 size_t workspace_bytes, void *stream) {
+    // checked before w_dtype is passed on as an enum value
+    if (!valid_dtype(w_dtype)) return fail(GPTQ_EINVAL, "w_dtype must be GPTQ_F32 or GPTQ_BF16");
     return gptq_quantize_layers(1, &W, w_dtype, &d_out, d_in, H, bits, group_size, block_size, damp, act_order,
                                 &Qpacked, &scales, &zeros, perm, workspace, workspace_bytes, stream);
 }
@@ -461,7 +481,7 @@ gptq_status gptq_quantize_layers(int n_layers, const void *const *W, gptq_dtype 
             Lmax = Ll;
         }
     }
-    if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "w_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (!valid_dtype(w_dtype)) return fail(GPTQ_EINVAL, "w_dtype must be GPTQ_F32 or GPTQ_BF16");
     if (!std::isfinite(damp) || damp < 0.f) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
     if (act_order != 0 && act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
     if (!H || !perm) return fail(GPTQ_EINVAL, "a required pointer is NULL");
@@ -502,8 +522,8 @@ gptq_status gptq_dequant_matmul(const void *A, gptq_dtype a_dtype, int64_t m, in
     int g = 0;
     gptq_status s = check_dequant(m, d_out, d_in, bits, group_size, g);
     if (s != GPTQ_OK) return s;
-    if (a_dtype != GPTQ_F32 && a_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "a_dtype must be GPTQ_F32 or GPTQ_BF16");
-    if (y_dtype != GPTQ_F32 && y_dtype != GPTQ_BF16) return fail(GPTQ_EINVAL, "y_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (!valid_dtype(a_dtype)) return fail(GPTQ_EINVAL, "a_dtype must be GPTQ_F32 or GPTQ_BF16");
+    if (!valid_dtype(y_dtype)) return fail(GPTQ_EINVAL, "y_dtype must be GPTQ_F32 or GPTQ_BF16");
     if (m == 0) return GPTQ_OK;
     if (!A || !Qpacked || !scales || !zeros || !Y) return fail(GPTQ_EINVAL, "a required pointer is NULL");
     const gptq::DequantWs wl = gptq::dequant_ws_layout(m, d_out, d_in, bits);

@@ -14,7 +14,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for b > 0, exact for every int64 a (no intermediate overflow)
+static inline int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b > 0); }
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
