@@ -187,6 +187,75 @@ def gemv_bench(P, torch, wl, q, Xd, calls=200):
     return out
 
 
+def other_workloads(P, torch, np, synth, skip):
+    """Every other configuration of the layer, timed in the same run: inputs
+    from the same seeded generator, resident in HBM; one untimed step, then a
+    few timed ones (two for the 70B layer).  Per workload: ms per layer,
+    TFLOP/s (Hessian + update flops), the Hessian product's average launch
+    time (library hipEvents) and fraction of its peak, and the layer's
+    roofline fraction (from one more step with every stage timed)."""
+    out = {}
+    dev = "cuda:0"
+    for name, wl in synth.WORKLOADS.items():
+        if name == skip:
+            continue
+        steps = 2 if wl.d_in > 16384 else 3
+        t0 = time.perf_counter()
+        W, X = synth.make_w(wl), synth.make_x(wl)
+
+        def to_dev(a):
+            if wl.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        Xd, Wd = to_dev(X), to_dev(W)
+        del W, X
+        H = torch.zeros(wl.d_in, wl.d_in, dtype=torch.float32, device=dev)
+        code = P.BF16 if wl.dtype == "bf16" else P.F32
+        ws_h = torch.empty(max(P.hessian_workspace_size(wl.n, wl.d_in, code), 1), dtype=torch.uint8, device=dev)
+        ws_q = torch.empty(P.quantize_layer_workspace_size(wl.d_out, wl.d_in, wl.bits, wl.group_size,
+                                                           wl.block_size, wl.act_order), dtype=torch.uint8, device=dev)
+
+        def step():
+            H.zero_()
+            P.hessian_accumulate(Xd, H, workspace=ws_h)
+            return P.quantize_layer(Wd, H, wl.bits, wl.group_size, wl.block_size, wl.damp, wl.act_order,
+                                    workspace=ws_q)
+
+        step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        P.profile_enable(1 << STAGE_HESSIAN_PRODUCT)
+        P.profile_read(reset=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        ms_h, n_h = P.profile_read(reset=True)["hessian_product"]
+        P.profile_enable(True)
+        step()
+        torch.cuda.synchronize()
+        prof = P.profile_read(reset=True)
+        P.profile_enable(False)
+        stages = {k: {"ms_per_step": v[0], "launches_per_step": v[1]} for k, v in prof.items()}
+        f_h, f_upd = workload_flops(wl)
+        avg_h = ms_h / max(n_h, 1)
+        peak_h = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+        out[name] = {"workload": describe(wl), "steps": steps, "ms_per_step": ms,
+                     "tflops": (f_h + f_upd) / (ms * 1e-3) / 1e12,
+                     "hessian_product": {"avg_launch_ms": avg_h, "achieved_tflops": f_h / (avg_h * 1e9),
+                                         "peak_tflops": peak_h, "frac": f_h / (avg_h * 1e9) / peak_h},
+                     "layer_roofline_frac": layer_roofline(wl, stages, ms)["frac"],
+                     "stages_ms": {k: v["ms_per_step"] for k, v in stages.items()}}
+        log(f"bench: {name}: {ms:.2f} ms per layer ({time.perf_counter() - t0:.1f} s with generation)")
+        del Xd, Wd, H, ws_h, ws_q
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, W, X):
     """The float64 oracle on a bounded sample of the same workload, scaled to
     the whole layer: Hessian over n_s tokens (scaled by n / n_s), the inverse
@@ -322,6 +391,8 @@ def main():
     ap.add_argument("--workload", default="q_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true", help="skip the product with the packed layer")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the other layer configurations after the headline one")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -424,6 +495,10 @@ def main():
     if not args.no_gemv:
         gemv = gemv_bench(P, torch, wl, step(), Xd)
 
+    others = None
+    if not args.no_other_workloads:
+        others = other_workloads(P, torch, np, synth, wl.name)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on a bounded sample")
@@ -443,6 +518,7 @@ def main():
         "layer_roofline": layer_roofline(wl, stages, ms_step),
         "dequant_gemv": gemv,
         "stages": stages,
+        "other_workloads": others,
         "flops": {"hessian": f_h, "update": f_upd},
     }
     print(json.dumps(line), flush=True)
