@@ -622,20 +622,19 @@ __device__ __forceinline__ void quant_one_block(const QuantArgs &a, int b, int e
     }
 }
 
-// BATCH: one launch takes nblocks blocks of width B from b0 (the blocks
-// between two far updates): each group takes its 16 rows through all of them.
-// Nothing crosses groups within a batch (a block's near update uses this
-// group's own earlier errors), so the blocks need no grid-wide
-// synchronization.  The loop keeps the kernel's arguments live across the
-// whole body (≈ 340 VGPRs, one group per SIMD set), so it is used when the grid
-// fits in one group per CU; otherwise one launch per block (nblocks = 1).
+// One launch takes nblocks blocks of width B from b0 (the blocks between two
+// far updates): each group takes its 16 rows through all of them.  Nothing
+// crosses groups within a batch (a block's near update uses this group's own
+// earlier errors), so the blocks need no grid-wide synchronization, and a
+// grid larger than the CUs simply runs in several rounds of whole batches.
+// (One launch per block instead, with its own rounds, was slower where the
+// grid exceeds the CUs: up_proj's in-block stage 2.22 -> 2.05 ms batched.)
 // a.E / a.En: the batch's error slots ([k][d_out], block t at rows t*B);
 // a.near_row0: the batch's first column.
 // Grid: ceil(d_out / 16) groups of 256 threads.
-template <bool BATCH>
 __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a, int b0, int nblocks, int B) {
     Quantizer Q = reuse_quantizer(1.f, 0.f, (float)((1 << a.bits) - 1));
-    for (int t = 0; t < (BATCH ? nblocks : 1); ++t) {
+    for (int t = 0; t < nblocks; ++t) {
         QuantArgs ab = a;
         const int b = b0 + t * B;
         const int e = (int)std::min<int64_t>(b + B, ab.d_in);
@@ -666,27 +665,11 @@ static size_t quant_launch_lds(int64_t d_in, int64_t b0, int nblocks, int64_t B)
     return std::max(quant_lds_bytes(w_first), quant_lds_bytes(w_last));
 }
 
-int quant_cu_count() {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-            cached = cus;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64_t B, hipStream_t st) {
     static bool attr_done = false;
     if (!attr_done) {
-        hipError_t err = hipFuncSetAttribute((const void *)quant_block_kernel<true>,
+        hipError_t err = hipFuncSetAttribute((const void *)quant_block_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (err == hipSuccess)
-            err = hipFuncSetAttribute((const void *)quant_block_kernel<false>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (err != hipSuccess) return err;
         attr_done = true;
     }
@@ -696,24 +679,12 @@ hipError_t quant_block_launch(const QuantArgs &a, int64_t b0, int nblocks, int64
     // ring_ok: the allocation holds the near-update ring after a 128-wide
     // block's staging (the kernel takes the ring only then)
     const size_t ring_need = quant_lds_bytes(128);
-    if ((int64_t)grid <= quant_cu_count()) {
-        const size_t lds = quant_launch_lds(a.d_in, b0, nblocks, B);
-        if (lds > 160 * 1024) return hipErrorInvalidValue;
-        QuantArgs ar = a;
-        ar.ring_ok = lds >= ring_need;
-        quant_block_kernel<true><<<grid, 256, lds, st>>>(ar, (int)b0, nblocks, (int)B);
-        return hipGetLastError();
-    }
-    for (int t = 0; t < nblocks; ++t) {
-        const size_t lds = quant_launch_lds(a.d_in, b0 + t * B, 1, B);
-        if (lds > 160 * 1024) return hipErrorInvalidValue;
-        QuantArgs ar = a;
-        ar.ring_ok = lds >= ring_need;
-        quant_block_kernel<false><<<grid, 256, lds, st>>>(ar, (int)(b0 + t * B), 1, (int)B);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    const size_t lds = quant_launch_lds(a.d_in, b0, nblocks, B);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    QuantArgs ar = a;
+    ar.ring_ok = lds >= ring_need;
+    quant_block_kernel<<<grid, 256, lds, st>>>(ar, (int)b0, nblocks, (int)B);
+    return hipGetLastError();
 }
 
 }  // namespace gptq

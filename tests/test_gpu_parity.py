@@ -197,10 +197,10 @@ LAYER_CASES = [
     ("up_proj", 310, 33, 250, 1500, 3, 16, 80, True),          # odd block, group 16
     ("q_proj", 311, 40, 1536, 3000, 4, 512, 512, False),       # groups of 512 over two 256-column internal blocks
     ("down_proj", 312, 24, 2304, 3000, 4, 768, 768, True),     # groups of 768 over three internal blocks
-    ("q_proj", 314, 4200, 384, 2048, 4, 128, 128, False),      # more row groups than CUs: one launch per block
+    ("q_proj", 314, 4200, 384, 2048, 4, 128, 128, False),      # more row groups than CUs: rounds of whole batches
     ("down70b", 315, 64, 384, 2048, 4, 128, 256, False),       # a 128-wide last block after a 256-wide one
     ("q_proj", 316, 48, 320, 2048, 4, 64, 192, False),         # the same after a 192-wide block
-    ("q_proj", 321, 4100, 384, 2048, 4, 128, 256, False),      # ... with one launch per block
+    ("q_proj", 321, 4100, 384, 2048, 4, 128, 256, False),      # ... with a 128-wide last block
     ("q_proj", 317, 64, 1300, 3000, 4, 256, 256, False),       # groups of 256, ragged last group
     ("q_proj", 318, 40, 2560, 4096, 4, 1024, 1024, False),     # groups of 1024 over four internal blocks
     ("up_proj", 319, 96, 768, 4096, 4, 32, 128, True, 0.005),  # 4-bit, groups of 32, act-order, damp 0.005
