@@ -363,18 +363,32 @@ int gemv_waves(int M, int64_t d_out, int64_t d_in, int bits) {
     return (M == 1 && packed < ((int64_t)16 << 20)) ? 8 : 4;
 }
 
-// work groups along k for a launch of M activation rows: about 128 work
-// groups in all for layers under 16 MB of packed words (fixed costs per group
-// dominate there) and 512 above, each wave with at least one unit, the staged
-// range within LDS (measured on q_proj, up_proj and the 70B down_proj)
+// work groups along k for a launch of M activation rows (measured on q_proj,
+// up_proj, down_proj and the 70B down_proj): about 128 work groups in all for
+// layers under 16 MB of packed words (fixed costs per group dominate there)
+// and 512 above.  With eight rows (more arithmetic per word) at most one group
+// per CU, 256 in all, unless a wave would then take more than 16 units, where
+// 512 (two per CU) hide the longer streams better; with two or four rows the
+// same only where it keeps at least 240 of the CUs busy.  A count just above
+// the CU count is the one to avoid: the CUs that take two groups finish last
+// (up_proj, 8 rows: 258 groups 54 us, 172 groups 40 us).  Each wave gets at
+// least one unit and the staged range fits in LDS.
 int gemv_splits(int M, int64_t d_out, int64_t d_in, int bits) {
     const int nunits = (int)cdiv(d_in, UNIT);
     const int64_t tiles = cdiv(d_out, GV_ROWS);
     const int max_units = GV_LDS / (M * UNIT);
+    const int waves = gemv_waves(M, d_out, d_in, bits);
     const int64_t packed = d_out * cdiv((int64_t)bits * d_in, 32) * 4;
-    const int64_t target = packed < ((int64_t)16 << 20) ? 128 : 512;
+    int64_t target = packed < ((int64_t)16 << 20) ? 128 : 512;
+    if (M > 1) {
+        const int64_t s1 = std::max<int64_t>(1, 256 / tiles);
+        if (nunits / s1 > 16 * waves)
+            target = 512;
+        else if (M == GV_MAX_M || s1 * tiles >= 240)
+            target = 256;
+    }
     int64_t s = std::max<int64_t>(1, target / tiles);
-    s = std::min<int64_t>(s, std::max(1, nunits / gemv_waves(M, d_out, d_in, bits)));
+    s = std::min<int64_t>(s, std::max(1, nunits / waves));
     s = std::max<int64_t>(s, cdiv(nunits, max_units));
     return (int)s;
 }
