@@ -1141,14 +1141,17 @@ bool gemm_ring_ok(int kc, int64_t d_in, int64_t d_out, int bits, int g) {
            bits * (d_in / 32) * d_out * 4 < lim && (d_in / 16) * d_out * 4 < lim;
 }
 
-// k splits of the wide path for a small grid (fewer tiles than half the
-// CUs), each split at least four stages of 32: at most
-// this many (the workspace holds their partial sums); a launch may take
-// fewer so that splits hold whole groups
+// k splits of the wide path for a small grid (fewer tiles than CUs), each
+// split at least four stages of 32 and at most GR_MAX_SPLIT (the workspace
+// holds their partial sums); a launch may take fewer so that splits hold
+// whole groups
 int gemm_splits(int64_t m, int64_t d_out, int64_t d_in) {
     const int64_t tiles = cdiv(m, GM_BM) * cdiv(d_out, GM_BN);
-    if (tiles >= 128) return 1;
-    int64_t s = cdiv(256, tiles);
+    if (tiles >= 256) return 1;
+    // the most splits that still fit one round of the CUs: a count just above
+    // it (ceil(256 / tiles) groups per tile) leaves a second, nearly empty
+    // round, and a round of 128 tiles alone leaves half the CUs idle
+    int64_t s = std::max<int64_t>(1, 256 / tiles);
     s = std::min<int64_t>(s, std::max<int64_t>(1, d_in / 32 / 4));
     return (int)std::min<int64_t>(s, GR_MAX_SPLIT);
 }
