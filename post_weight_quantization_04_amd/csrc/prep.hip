@@ -35,23 +35,32 @@ __global__ __launch_bounds__(1024) void diag_lambda_kernel(const float *__restri
 // and i < j.  That is a strict total order, so the ranks form a permutation.
 __device__ __forceinline__ float order_key(float v) { return (v != v) ? -__builtin_huge_valf() : v; }
 
-constexpr int RANK_TILE = 1024;
+constexpr int RANK_TILE = 256;
 
-// rank[i] += #{j in this group's slice : j precedes i}
+// rank[i] += #{j in this group's slice : j precedes i}.  The slice's keys go
+// to LDS, padded with -inf past d (a padded j >= d never precedes any i < d),
+// and are read back four at a time.  Slices of 256 give d = 4096 a grid of
+// 256 groups; with slices of 1024 read one key per step, the 64 groups of
+// that size waited on LDS for every comparison (≈ 120 us at d = 4096).
 __global__ __launch_bounds__(256) void rank_kernel(const float *__restrict__ dg, int64_t d,
                                                    int32_t *__restrict__ rank) {
-    __shared__ float kj[RANK_TILE];
+    __shared__ __attribute__((aligned(16))) float kj[RANK_TILE];
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t j0 = (int64_t)blockIdx.y * RANK_TILE;
-    const int64_t j1 = std::min<int64_t>(d, j0 + RANK_TILE);
-    for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) kj[j - j0] = order_key(dg[j]);
+    for (int t = threadIdx.x; t < RANK_TILE; t += 256)
+        kj[t] = (j0 + t < d) ? order_key(dg[j0 + t]) : -__builtin_huge_valf();
     __syncthreads();
     if (i >= d) return;
     const float ki = order_key(dg[i]);
     int cnt = 0;
-    for (int64_t j = j0; j < j1; ++j) {
-        const float v = kj[j - j0];
-        cnt += (v > ki) || (v == ki && j < i);
+#pragma unroll 8
+    for (int t = 0; t < RANK_TILE; t += 4) {
+        const f32x4 v = *(const f32x4 *)(kj + t);
+        const int64_t j = j0 + t;
+        cnt += (v.x > ki) || (v.x == ki && j + 0 < i);
+        cnt += (v.y > ki) || (v.y == ki && j + 1 < i);
+        cnt += (v.z > ki) || (v.z == ki && j + 2 < i);
+        cnt += (v.w > ki) || (v.w == ki && j + 3 < i);
     }
     if (cnt) atomicAdd(rank + i, cnt);
 }
