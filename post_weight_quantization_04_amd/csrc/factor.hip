@@ -703,21 +703,16 @@ __device__ __forceinline__ void diag_quadrant(float *__restrict__ R, int64_t d, 
     }
     // every read goes out before the first product
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 acc;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        acc[4 * a + 0] = -cv[a].x;
-        acc[4 * a + 1] = -cv[a].y;
-        acc[4 * a + 2] = -cv[a].z;
-        acc[4 * a + 3] = -cv[a].w;
-    }
+    // the 128-term sums apart from C, applied to it once
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < 64; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[s >> 2][s & 3], av[s >> 2][s & 3], acc, 0, 0, 0);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int c = cb + 8 * a + 4 * h;
-        const f32x4 x = {-acc[4 * a + 0], -acc[4 * a + 1], -acc[4 * a + 2], -acc[4 * a + 3]};
+        const f32x4 x = {cv[a].x - acc[4 * a + 0], cv[a].y - acc[4 * a + 1], cv[a].z - acc[4 * a + 2],
+                         cv[a].w - acc[4 * a + 3]};
         if (r < rows) {
             if (c + 3 < rows) {
                 *(f32x4 *)(Crow + c) = x;
@@ -804,20 +799,22 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float *__restrict__ R, i
     float *C = R + (int64_t)row0 * d + col0;
     const float *A = panel + (int64_t)(row0 - k1) * NB;       // A(m, k) = P[row0+m][k]
     f32x16 acc[4];
+    zero_acc(acc);
     if (j == k) {
-        zero_acc(acc);
         // B(k, n) = Dinv[k][n]: n-contiguous
         gemm_tile<true, false>(acc, A, NB, dinv_k, NB, rows, cols, kb, 1.f, true, lds);
-    } else if (j < k) {
-        load_c(acc, C, d, rows, cols);
+        store_c(acc, C, d, rows, cols);
+        return;
+    }
+    // the products summed apart from C, added to it once
+    if (j < k) {
         const float *B = R + (int64_t)k0 * d + col0;           // M[k0+k][col0+n]
         gemm_tile<true, false>(acc, A, NB, B, d, rows, cols, kb, 1.f, aligned16(B, d), lds);
     } else {
-        load_c(acc, C, d, rows, cols);
         const float *B = panel + (int64_t)(col0 - k1) * NB;    // B(k, n) = P[col0+n][k]
         gemm_tile<true, true>(acc, A, NB, B, NB, rows, cols, kb, -1.f, true, lds);
     }
-    store_c(acc, C, d, rows, cols);
+    add_store_c(acc, C, d, rows, cols);
 }
 
 // Far update of the batch of steps s .. e-1 (e < nblk), one 128 x 128 tile

@@ -101,6 +101,16 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[4], float *C, int64_
             }
 }
 
+// C += acc on the tile: the products are summed apart from C and applied to
+// it once, one rounding onto C per step instead of one per MFMA.
+__device__ __forceinline__ void add_store_c(const f32x16 (&acc)[4], float *C, int64_t ldc, int rows, int cols) {
+    f32x16 cur[4];
+    load_c(cur, C, ldc, rows, cols);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] += acc[i];
+    store_c(cur, C, ldc, rows, cols);
+}
+
 // One operand chunk: 32 (k) x 128 (m or n) values held as 16 floats per thread.
 // KCONTIG: the source is contiguous along k (element (m, k) at p[m*ld + k]).
 template <bool KCONTIG>
